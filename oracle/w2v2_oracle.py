@@ -1,0 +1,326 @@
+"""Plain CPU oracle of wav2vec2-CTC encoder inference.
+
+TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct
+definition that the HIP library is checked against.  Only the test suite,
+the smoke check and the benchmark's CPU-baseline leg may import it; the
+product path (the C-ABI library and its Python binding) never does, and this
+module imports nothing from that path.
+
+It computes the network exactly as defined, in float64 by default (any
+numpy float dtype can be passed to bound its own rounding), with the
+feature encoder in [B, C, T] layout and every step written as its textbook
+definition.  Library primitives used as steps: ``numpy.matmul`` (a matrix
+product) and ``scipy.special.erf``.
+
+Sources (cited by page title and section):
+
+* "litert-community/wav2vec2-base-960h-LiteRT - discussion #1" (Hugging Face):
+  sections "Recipe", "Rewrites for the GPU", "fp16 / int8".
+* "TensorRT-Model-Connect, families/wav2vec2/README.md": intro "Wav2Vec2 CTC
+  layouts", "FP8 quantization study", "Recipe that was measured", "Method",
+  "Results".
+
+Where the pages leave a step open, the reading taken is stated at the step.
+
+Parity pins: every function here is pinned by a ``-m "not gpu"`` test
+against something other than itself (closed forms, brute-force loops,
+invariants, an independent library implementation of the same network);
+no function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.special import erf as _erf
+
+
+# ----------------------------------------------------------------------------
+# elementwise pieces
+# ----------------------------------------------------------------------------
+def gelu(x: np.ndarray) -> np.ndarray:
+    """Exact GELU, x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)).
+
+    The LiteRT discussion ("Rewrites for the GPU") calls its tanh-GELU rewrite
+    the only non-exact step of its export, so the model's own GELU is the
+    erf form; it is used for the conv feature encoder, the positional conv
+    and the feed-forward block alike.
+    """
+    x = np.asarray(x)
+    return 0.5 * x * (1.0 + _erf(x / np.sqrt(x.dtype.type(2.0))))
+
+
+def layer_norm(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float,
+               axis: int = -1) -> np.ndarray:
+    """LayerNorm over ``axis``: biased variance, eps inside the square root."""
+    mu = x.mean(axis=axis, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=axis, keepdims=True)
+    shape = [1] * x.ndim
+    shape[axis] = -1
+    return (x - mu) / np.sqrt(var + eps) * gamma.reshape(shape) + beta.reshape(shape)
+
+
+def group_norm_over_time(y: np.ndarray, gamma: np.ndarray, beta: np.ndarray,
+                         eps: float) -> np.ndarray:
+    """GroupNorm with one group per channel on y [B, C, T].
+
+    TensorRT README, "Results": the feature encoder's first normalization is
+    "a group norm over every time step of the clip".  Reading: groups = C,
+    so the statistics are per (b, c) over all T frames of the padded window.
+    """
+    mu = y.mean(axis=2, keepdims=True)
+    var = ((y - mu) ** 2).mean(axis=2, keepdims=True)
+    return (y - mu) / np.sqrt(var + eps) * gamma[None, :, None] + beta[None, :, None]
+
+
+# ----------------------------------------------------------------------------
+# convolutions
+# ----------------------------------------------------------------------------
+def conv_out_len(length: int, kernel: int, stride: int) -> int:
+    """Frames of an unpadded strided conv: floor((L - K) / s) + 1, 0 if L < K."""
+    return 0 if length < kernel else (length - kernel) // stride + 1
+
+
+def conv1d(x: np.ndarray, w: np.ndarray, b: np.ndarray | None, stride: int) -> np.ndarray:
+    """Unpadded strided conv1d on x [B, C_in, L], w [C_out, C_in, K].
+
+    y[b, o, t] = bias[o] + sum_k sum_c w[o, c, k] * x[b, c, s*t + k],
+    written as one matrix product per tap k.
+    """
+    bsz, c_in, length = x.shape
+    c_out, c_in_w, kernel = w.shape
+    assert c_in == c_in_w
+    t_out = conv_out_len(length, kernel, stride)
+    y = np.zeros((bsz, c_out, t_out), dtype=x.dtype)
+    if t_out == 0:
+        return y
+    for k in range(kernel):
+        xs = x[:, :, k:k + stride * (t_out - 1) + 1:stride]          # [B, C_in, T]
+        y += np.matmul(w[:, :, k], xs)                                # [C_out, C_in] @ [B, C_in, T]
+    if b is not None:
+        y += b[None, :, None]
+    return y
+
+
+def fold_weight_norm(v: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """Weight norm w = g * v / ||v||.
+
+    LiteRT discussion, "Rewrites for the GPU": the positional conv carries a
+    weight norm g*v/||v||.  Reading (the pages name no axis): one norm per
+    kernel tap k, taken over all output and input channels of that tap, so
+    g has one entry per tap.
+    """
+    norm = np.sqrt((v ** 2).sum(axis=(0, 1)))                            # [K]
+    return v * (g.reshape(-1) / norm)[None, None, :]
+
+
+def positional_conv(z: np.ndarray, w: np.ndarray, b: np.ndarray, groups: int) -> np.ndarray:
+    """Grouped positional conv on z [B, T, d]; w [d, d/G, K] (already folded).
+
+    p[b, t, o] = bias[o] + sum_k sum_i w[o, i, k] * zpad[b, t + k, g(o)*d/G + i]
+    with zpad = z padded by K//2 zero frames on both sides.  Reading for even
+    K (the pages are silent): the padded conv yields T + 1 frames and the
+    last one is dropped, so frame t sees z[t - K/2 .. t + K/2 - 1].
+    """
+    bsz, t_len, d = z.shape
+    c_out, cg, kernel = w.shape
+    assert c_out == d and cg * groups == d
+    pad = kernel // 2
+    zp = np.zeros((bsz, t_len + 2 * pad, d), dtype=z.dtype)
+    zp[:, pad:pad + t_len] = z
+    t_full = t_len + 2 * pad - kernel + 1
+    zg = zp.reshape(bsz, t_len + 2 * pad, groups, cg).transpose(2, 0, 1, 3)  # [G, B, Tp, Cg]
+    wg = w.reshape(groups, cg, cg, kernel)                                  # [G, o, i, K]
+    p = np.zeros((groups, bsz, t_full, cg), dtype=z.dtype)
+    for k in range(kernel):
+        a = zg[:, :, k:k + t_full, :].reshape(groups, bsz * t_full, cg)
+        p += np.matmul(a, wg[:, :, :, k].transpose(0, 2, 1)).reshape(groups, bsz, t_full, cg)
+    p = p.transpose(1, 2, 0, 3).reshape(bsz, t_full, d)
+    if kernel % 2 == 0:
+        p = p[:, :t_len]
+    return p + b[None, None, :]
+
+
+# ----------------------------------------------------------------------------
+# transformer pieces
+# ----------------------------------------------------------------------------
+def softmax(s: np.ndarray, axis: int = -1) -> np.ndarray:
+    """softmax(s)_j = exp(s_j) / sum exp(s); the row max is subtracted first,
+    which leaves the value unchanged."""
+    m = s.max(axis=axis, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=axis, keepdims=True)
+
+
+def self_attention(h: np.ndarray, W: dict, prefix: str, heads: int) -> np.ndarray:
+    """Multi-head self-attention over all T frames, no mask.
+
+    LiteRT discussion, "Rewrites for the GPU": the bidirectional mask is
+    removed, so attention is plain scaled dot-product attention over the
+    whole window (short clips are zero-padded).  q/k/v/out projections carry
+    biases (TensorRT README, "Recipe that was measured", lists q_proj,
+    k_proj, v_proj, out_proj).  Scale 1/sqrt(d_head).
+    """
+    bsz, t_len, d = h.shape
+    dh = d // heads
+    dt = h.dtype
+
+    def proj(name: str, x: np.ndarray) -> np.ndarray:
+        return np.matmul(x, W[prefix + name + ".weight"].astype(dt).T) + W[prefix + name + ".bias"].astype(dt)
+
+    q = proj("q", h).reshape(bsz, t_len, heads, dh).transpose(0, 2, 1, 3)
+    k = proj("k", h).reshape(bsz, t_len, heads, dh).transpose(0, 2, 1, 3)
+    v = proj("v", h).reshape(bsz, t_len, heads, dh).transpose(0, 2, 1, 3)
+    s = np.matmul(q, k.transpose(0, 1, 3, 2)) / np.sqrt(dt.type(dh))   # [B, H, T, T]
+    o = np.matmul(softmax(s, axis=-1), v)                               # [B, H, T, dh]
+    o = o.transpose(0, 2, 1, 3).reshape(bsz, t_len, d)
+    return proj("out", o)
+
+
+def feed_forward(h: np.ndarray, W: dict, prefix: str) -> np.ndarray:
+    """fc2(GELU(fc1(h))), both linears with bias (TensorRT README, "Recipe that
+    was measured": intermediate_dense and output_dense)."""
+    dt = h.dtype
+    u = np.matmul(h, W[prefix + "fc1.weight"].astype(dt).T) + W[prefix + "fc1.bias"].astype(dt)
+    return np.matmul(gelu(u), W[prefix + "fc2.weight"].astype(dt).T) + W[prefix + "fc2.bias"].astype(dt)
+
+
+# ----------------------------------------------------------------------------
+# network
+# ----------------------------------------------------------------------------
+def num_frames(cfg, samples: int) -> int:
+    """Output frames of the conv feature encoder for ``samples`` input
+    samples: the unpadded conv length rule applied layer by layer."""
+    n = int(samples)
+    for k, s in zip(cfg.conv_kernel, cfg.conv_stride):
+        n = conv_out_len(n, k, s)
+    return n
+
+
+def feature_encoder(cfg, W: dict, pcm: np.ndarray, valid: np.ndarray,
+                    dtype=np.float64) -> np.ndarray:
+    """Conv feature encoder: PCM [B, L] -> features [B, C, T].
+
+    * Samples at or after valid[b] are taken as exact zeros, whatever the
+      buffer holds (LiteRT discussion, "Rewrites for the GPU": short clips
+      are zero-padded to the fixed window).
+    * Group-norm variant: conv0 -> GroupNorm over time -> GELU, then
+      conv_i -> GELU.  Layer-norm variant: every conv_i -> LayerNorm over the
+      channels of each frame -> GELU.  Conv bias only where the config has it
+      (TensorRT README, "Wav2Vec2 CTC layouts": group-normalized and per-frame
+      layer-normalized feature encoders, with or without convolution bias).
+    """
+    dt = np.dtype(dtype)
+    x = np.asarray(pcm, dtype=dt).copy()
+    for b in range(x.shape[0]):
+        x[b, int(valid[b]):] = 0.0
+    h = x[:, None, :]
+    for i in range(len(cfg.conv_dim)):
+        wk = W[f"fe.conv{i}.weight"].astype(dt)
+        bk = W[f"fe.conv{i}.bias"].astype(dt) if cfg.conv_bias else None
+        h = conv1d(h, wk, bk, cfg.conv_stride[i])
+        if cfg.feat_norm == "layer":
+            h = layer_norm(h, W[f"fe.norm{i}.weight"].astype(dt), W[f"fe.norm{i}.bias"].astype(dt),
+                           cfg.eps, axis=1)
+        elif i == 0:
+            h = group_norm_over_time(h, W["fe.norm0.weight"].astype(dt), W["fe.norm0.bias"].astype(dt),
+                                     cfg.eps)
+        h = gelu(h)
+    return h
+
+
+def encoder(cfg, W: dict, feats: np.ndarray) -> np.ndarray:
+    """Feature projection, positional conv and the transformer blocks.
+
+    feats [B, C, T] -> hidden [B, T, d].
+
+    * Feature projection: LayerNorm over C per frame, then Linear C -> d.
+    * Positional conv: h = z + GELU(posconv(z)), with the weight norm folded
+      from (v, g) on every call (LiteRT discussion, "Rewrites for the GPU").
+    * Post-norm blocks (TensorRT README, "Wav2Vec2 CTC layouts": blocks keep
+      the checkpoint's post-norm or stable pre-norm order; stable checkpoints
+      apply the encoder-level norm after the blocks; reading: the post-norm
+      layout applies it before them):
+        h = LN(h);  per block: h = LN(h + MHA(h)); h = LN(h + FFN(h)).
+      Stable pre-norm:
+        per block: h = h + MHA(LN(h)); h = h + FFN(LN(h));  then h = LN(h).
+    """
+    dt = feats.dtype
+    eps = cfg.eps
+
+    def g(name):
+        return W[name].astype(dt)
+
+    f = feats.transpose(0, 2, 1)                                         # [B, T, C]
+    f = layer_norm(f, g("fp.norm.weight"), g("fp.norm.bias"), eps)
+    z = np.matmul(f, g("fp.proj.weight").T) + g("fp.proj.bias")
+    w_pos = fold_weight_norm(g("pos.weight_v"), g("pos.weight_g"))
+    h = z + gelu(positional_conv(z, w_pos, g("pos.bias"), cfg.pos_groups))
+    if not cfg.stable_layer_norm:
+        h = layer_norm(h, g("enc.norm.weight"), g("enc.norm.bias"), eps)
+    for l in range(cfg.layers):
+        p = f"layer{l}."
+        if cfg.stable_layer_norm:
+            a = layer_norm(h, g(p + "attn_norm.weight"), g(p + "attn_norm.bias"), eps)
+            h = h + self_attention(a, W, p + "attn.", cfg.heads)
+            a = layer_norm(h, g(p + "ffn_norm.weight"), g(p + "ffn_norm.bias"), eps)
+            h = h + feed_forward(a, W, p + "ffn.")
+        else:
+            h = layer_norm(h + self_attention(h, W, p + "attn.", cfg.heads),
+                           g(p + "attn_norm.weight"), g(p + "attn_norm.bias"), eps)
+            h = layer_norm(h + feed_forward(h, W, p + "ffn."),
+                           g(p + "ffn_norm.weight"), g(p + "ffn_norm.bias"), eps)
+    if cfg.stable_layer_norm:
+        h = layer_norm(h, g("enc.norm.weight"), g("enc.norm.bias"), eps)
+    return h
+
+
+def ctc_head(W: dict, h: np.ndarray) -> np.ndarray:
+    """CTC logits = h W^T + b over the vocabulary (TensorRT README, "Recipe
+    that was measured": the CTC head)."""
+    dt = h.dtype
+    return np.matmul(h, W["head.weight"].astype(dt).T) + W["head.bias"].astype(dt)
+
+
+def valid_frames(cfg, valid: np.ndarray) -> np.ndarray:
+    """Frames per row computed from valid samples only (LiteRT discussion,
+    "Rewrites for the GPU": decoding runs over the valid frames)."""
+    return np.array([num_frames(cfg, int(v)) for v in valid], dtype=np.int32)
+
+
+def forward(cfg, W: dict, pcm: np.ndarray, valid: np.ndarray, dtype=np.float64):
+    """Whole network: (logits [B, T, V] in ``dtype``, valid frames int32 [B]).
+
+    Logits are produced for every frame of the window; only the first
+    valid-frames of each row are decoded.
+    """
+    feats = feature_encoder(cfg, W, pcm, valid, dtype)
+    h = encoder(cfg, W, feats)
+    return ctc_head(W, h), valid_frames(cfg, valid)
+
+
+# ----------------------------------------------------------------------------
+# greedy CTC decoding
+# ----------------------------------------------------------------------------
+def frame_argmax(logits: np.ndarray) -> np.ndarray:
+    """Per-frame argmax over the vocabulary, lowest index on ties (the
+    per-frame argmax of LiteRT discussion "fp16 / int8" and TensorRT README
+    "Method").  int32 [..., T]."""
+    return np.argmax(logits, axis=-1).astype(np.int32)
+
+
+def ctc_collapse(path, blank: int) -> np.ndarray:
+    """Greedy (best-path) CTC collapse: merge runs of equal ids, then remove
+    the blank id.  Textbook CTC decoding rule (Graves et al., 2006)."""
+    out = []
+    prev = None
+    for a in path:
+        a = int(a)
+        if a != prev and a != blank:
+            out.append(a)
+        prev = a
+    return np.array(out, dtype=np.int32)
+
+
+def greedy_decode(logits: np.ndarray, vframes: np.ndarray, blank: int) -> list[np.ndarray]:
+    """Token ids per row: argmax over the valid frames, then collapse."""
+    a = frame_argmax(logits)
+    return [ctc_collapse(a[b, :int(vframes[b])], blank) for b in range(a.shape[0])]

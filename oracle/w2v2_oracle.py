@@ -93,8 +93,9 @@ def conv1d(x: np.ndarray, w: np.ndarray, b: np.ndarray | None, stride: int) -> n
     if t_out == 0:
         return y
     for k in range(kernel):
-        xs = x[:, :, k:k + stride * (t_out - 1) + 1:stride]          # [B, C_in, T]
-        y += np.matmul(w[:, :, k], xs)                                # [C_out, C_in] @ [B, C_in, T]
+        # contiguous copies only so that numpy's matmul takes its BLAS path
+        xs = np.ascontiguousarray(x[:, :, k:k + stride * (t_out - 1) + 1:stride])   # [B, C_in, T]
+        y += np.matmul(np.ascontiguousarray(w[:, :, k]), xs)                          # [C_out, C_in] @ [B, C_in, T]
     if b is not None:
         y += b[None, :, None]
     return y
@@ -132,7 +133,8 @@ def positional_conv(z: np.ndarray, w: np.ndarray, b: np.ndarray, groups: int) ->
     p = np.zeros((groups, bsz, t_full, cg), dtype=z.dtype)
     for k in range(kernel):
         a = zg[:, :, k:k + t_full, :].reshape(groups, bsz * t_full, cg)
-        p += np.matmul(a, wg[:, :, :, k].transpose(0, 2, 1)).reshape(groups, bsz, t_full, cg)
+        wk = np.ascontiguousarray(wg[:, :, :, k].transpose(0, 2, 1))     # [G, i, o]
+        p += np.matmul(np.ascontiguousarray(a), wk).reshape(groups, bsz, t_full, cg)
     p = p.transpose(1, 2, 0, 3).reshape(bsz, t_full, d)
     if kernel % 2 == 0:
         p = p[:, :t_len]

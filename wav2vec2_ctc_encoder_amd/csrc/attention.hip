@@ -1,0 +1,228 @@
+// Flash-style multi-head self-attention over all T frames (no mask), gfx950.
+//
+// Input: the fused projection output qkv [B*T, 3d] (q | k | v; head h at
+// columns h*dh of each part).  Output: o [B*T, d], heads concatenated.
+// out[q] = sum_key softmax_key(q.k / sqrt(dh)) v[key].
+//
+// Workgroup = 64 queries of one (batch row, head); 4 waves x 16 queries.
+// K and V are streamed through LDS in tiles of 64 keys (V stored
+// transposed, [d][key]); softmax is computed online in fp32 with exp2 and a
+// running max per query, so the T x T score matrix never leaves registers.
+//
+// Each wave computes the transposed score block S^T = K Q^T with 16x16 MFMA
+// blocks (A operand = 16 keys, B operand = 16 queries), so a lane holds the
+// scores of ONE query (lane % 16) for 4 keys per block.  That is exactly the
+// B-operand layout P^T needs for O^T = V^T P^T, the second product: the
+// scores are turned into probabilities in place and fed back to the matrix
+// core without any shuffle.  The MFMA k-slots of the second product carry
+// keys {16b + 4g + r}; the V^T operand reads the same keys from LDS, so the
+// contraction covers every key once.  Tail keys (>= T) get score -inf and
+// zero K/V rows.
+#include "common.h"
+
+namespace w2v2 {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+constexpr int kQ = 64;   // queries per workgroup
+constexpr int kKT = 64;  // keys per tile
+
+template <typename T, int DH>
+struct AttnCfg {
+  static constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
+  static constexpr int KC = 64 / sizeof(T);           // d per MFMA chunk (32 fp16, 16 fp32)
+  static constexpr int DHP = DH < KC ? KC : DH;       // d padded to whole chunks
+  static constexpr int NCH = DHP / KC;                // d chunks of the score product
+  static constexpr int KPITCH = DHP * sizeof(T) / 16 + 1;  // K row pitch, 16-byte units
+  static constexpr int VPITCH = kKT * sizeof(T) / 16 + 1;  // V^T row pitch, 16-byte units
+  static constexpr int ND = DH / 16;                  // 16-row d blocks of the output
+};
+
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qkv, T* __restrict__ out, int Tn,
+                                                        int H, float c1) {
+  using C = AttnCfg<T, DH>;
+  __shared__ uint4 sK[kKT * C::KPITCH];
+  __shared__ uint4 sV[DH * C::VPITCH];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int dm = H * DH;
+  const int64_t ld = 3 * (int64_t)dm;
+  const T* base = qkv + (int64_t)b * Tn * ld;
+  const int q0 = blockIdx.x * kQ + wave * 16;
+
+  // zero the padded d range of K once (only when DH < one MFMA chunk)
+  if (DH < C::DHP) {
+    for (int i = tid; i < kKT * C::KPITCH; i += 256) sK[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+  }
+
+  // Q fragments of this wave's 16 queries: lane (lr, lg), chunk c
+  uint4 qf[C::NCH];
+  {
+    const int q = q0 + lr;
+#pragma unroll
+    for (int c = 0; c < C::NCH; ++c) {
+      const int d0 = c * C::KC + lg * C::EPC;
+      qf[c] = (q < Tn && d0 < DH) ? *(const uint4*)(base + (int64_t)q * ld + h * DH + d0) : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  f4 o[C::ND];
+#pragma unroll
+  for (int i = 0; i < C::ND; ++i) o[i] = f4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lsum = 0.f;
+
+  constexpr int CPR = DH / C::EPC;  // 16-byte chunks per K/V row
+  for (int k0 = 0; k0 < Tn; k0 += kKT) {
+    __syncthreads();
+    for (int idx = tid; idx < kKT * CPR; idx += 256) {
+      const int r = idx / CPR, ch = idx % CPR;
+      const int key = k0 + r;
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (key < Tn) {
+        const T* row = base + (int64_t)key * ld + h * DH + ch * C::EPC;
+        kv = *(const uint4*)(row + dm);
+        vv = *(const uint4*)(row + 2 * dm);
+      }
+      sK[r * C::KPITCH + ch] = kv;
+      const T* ve = (const T*)&vv;
+      T* vt = (T*)sV;
+#pragma unroll
+      for (int e = 0; e < C::EPC; ++e) vt[(ch * C::EPC + e) * (C::VPITCH * C::EPC) + r] = ve[e];
+    }
+    __syncthreads();
+
+    // scores S^T[key][q] for 4 key blocks of 16
+    f4 s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < C::NCH; ++c) {
+        const uint4 kf = sK[(kb * 16 + lr) * C::KPITCH + c * 4 + lg];
+        if constexpr (sizeof(T) == 2) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, kf), __builtin_bit_cast(h8, qf[c]),
+                                                       acc, 0, 0, 0);
+        } else {
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf.x), __uint_as_float(qf[c].x), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf.y), __uint_as_float(qf[c].y), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf.z), __uint_as_float(qf[c].z), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf.w), __uint_as_float(qf[c].w), acc, 0, 0, 0);
+        }
+      }
+      s[kb] = acc;
+    }
+    // online softmax for query lr (4 lanes share it: lg = 0..3)
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0 + kb * 16 + lg * 4 + r;
+        if (key >= Tn) s[kb][r] = -INFINITY;
+        mt = fmaxf(mt, s[kb][r]);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mnew = fmaxf(mrun, mt);
+    const float alpha = exp2f((mrun - mnew) * c1);
+    const float mc = mnew * c1;
+    mrun = mnew;
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = exp2f(fmaf(s[kb][r], c1, -mc));
+        s[kb][r] = p;
+        ps += p;
+      }
+    lsum = lsum * alpha + ps;
+#pragma unroll
+    for (int i = 0; i < C::ND; ++i) o[i] *= alpha;
+
+    // O^T[d][q] += V^T[d][key] P^T[key][q]
+    const T* vt = (const T*)sV;
+#pragma unroll
+    for (int db = 0; db < C::ND; ++db) {
+      const T* vrow = vt + (db * 16 + lr) * (C::VPITCH * C::EPC);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          const h4 va = *(const h4*)(vrow + (2 * kp) * 16 + lg * 4);
+          const h4 vb = *(const h4*)(vrow + (2 * kp + 1) * 16 + lg * 4);
+          const h8 av = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+          const h8 pv = {(half_t)s[2 * kp][0], (half_t)s[2 * kp][1], (half_t)s[2 * kp][2], (half_t)s[2 * kp][3],
+                         (half_t)s[2 * kp + 1][0], (half_t)s[2 * kp + 1][1], (half_t)s[2 * kp + 1][2],
+                         (half_t)s[2 * kp + 1][3]};
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pv, o[db], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const float4 va = *(const float4*)(vrow + kb * 16 + lg * 4);
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.x, s[kb][0], o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.y, s[kb][1], o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.z, s[kb][2], o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.w, s[kb][3], o[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  const float inv = 1.f / lsum;
+  const int q = q0 + lr;
+  if (q < Tn) {
+    T* orow = out + ((int64_t)b * Tn + q) * dm + h * DH;
+#pragma unroll
+    for (int db = 0; db < C::ND; ++db) {
+      const int d0 = db * 16 + lg * 4;
+      if constexpr (sizeof(T) == 2) {
+        const h4 hv = {(half_t)(o[db][0] * inv), (half_t)(o[db][1] * inv), (half_t)(o[db][2] * inv),
+                       (half_t)(o[db][3] * inv)};
+        *(h4*)(orow + d0) = hv;
+      } else {
+        *(float4*)(orow + d0) = make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+      }
+    }
+  }
+}
+
+template <typename T, int DH>
+hipError_t launch_t(const void* qkv, void* out, int B, int Tn, int H, hipStream_t s) {
+  const float c1 = 1.4426950408889634f / sqrtf((float)DH);  // log2(e) / sqrt(dh)
+  hipLaunchKernelGGL((attention_kernel<T, DH>), dim3((Tn + kQ - 1) / kQ, H, B), dim3(256), 0, s,
+                     (const T*)qkv, (T*)out, Tn, H, c1);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dh(const void* qkv, void* out, int B, int Tn, int H, int dh, hipStream_t s) {
+  switch (dh) {
+    case 16: return launch_t<T, 16>(qkv, out, B, Tn, H, s);
+    case 32: return launch_t<T, 32>(qkv, out, B, Tn, H, s);
+    case 64: return launch_t<T, 64>(qkv, out, B, Tn, H, s);
+    case 128: return launch_t<T, 128>(qkv, out, B, Tn, H, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool attention_supported(int dh) { return dh == 16 || dh == 32 || dh == 64 || dh == 128; }
+
+hipError_t launch_attention(DType t, const void* qkv, void* out, int32_t B, int32_t T, int32_t H, int32_t dh,
+                            hipStream_t s) {
+  if (B <= 0 || T <= 0) return hipSuccess;
+  return t == DType::F16 ? launch_dh<half_t>(qkv, out, B, T, H, dh, s) : launch_dh<float>(qkv, out, B, T, H, dh, s);
+}
+
+}  // namespace w2v2

@@ -1,0 +1,112 @@
+// Internal declarations shared by the HIP kernels and the runtime.
+// Target: gfx950 (CDNA4), wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w2v2 {
+
+typedef _Float16 half_t;
+
+// Element type of matrix operands: fp16 in the fp16 mode, fp32 in the fp32 mode.
+enum class DType : int { F32 = 0, F16 = 1 };
+
+inline size_t dsize(DType t) { return t == DType::F16 ? 2 : 4; }
+
+// Kernel-timing hook of the runtime: called around every launch.
+struct LaunchHook {
+  virtual void before(const char* name, hipStream_t s) = 0;
+  virtual void after(const char* name, hipStream_t s) = 0;
+  virtual ~LaunchHook() {}
+};
+
+// ----------------------------------------------------------------------------
+// GEMM:  C[m, n] = epilogue( sum_k A[m, k] * Bw[n, k] )
+//   A rows are addressed through a two-level map so the same kernel serves
+//   linears, implicit-GEMM strided convs and the grouped positional conv:
+//     row m -> seg = m / seg_rows, t = m % seg_rows,
+//     A_row(m) = A + group*a_group + seg*a_seg + t*lda      (elements)
+//   Bw is [N, K] row-major per group (ldb = K): Bw + group*b_group.
+//   Epilogue per element: v = acc + bias[n]; v = act(v); v += residual[m, n];
+//   stores fp32 (out_f32) and/or operand type (out_t) at C + group*c_group + m*ldc + n.
+//   grid.z = groups.
+// ----------------------------------------------------------------------------
+struct GemmArgs {
+  const void* A = nullptr;
+  int64_t lda = 0, a_seg = 0, a_group = 0;
+  int32_t seg_rows = 1;
+  const void* B = nullptr;
+  int64_t b_group = 0;
+  int32_t M = 0, N = 0, K = 0, groups = 1;
+  const float* bias = nullptr;
+  int64_t bias_group = 0;
+  const float* residual = nullptr;  // fp32, indexed like C; may alias out_f32
+  float* out_f32 = nullptr;
+  void* out_t = nullptr;
+  int64_t ldc = 0, c_group = 0;
+  int32_t act = 0;  // 0 none, 1 exact GELU
+};
+
+// Tile shape is chosen from N: 128x32, 128x48, 128x64 or 128x128.
+hipError_t launch_gemm(DType t, const GemmArgs& a, hipStream_t s);
+
+// ----------------------------------------------------------------------------
+// feature-encoder kernels
+// ----------------------------------------------------------------------------
+// conv 0 (one input channel) over the zero-padded window.
+//   pcm [B, L] fp32, valid [B]; w0 [C][k] fp32; bias [C] fp32 or null.
+//   group variant (stats != null): y [B, T0, C] (type t) = conv, plus per
+//     (b, chunk, c) partial (mean, M2) over the chunk's frames.
+//   layer variant (gamma != null): y = GELU(LN_c(conv + bias) * gamma + beta).
+int conv0_chunk_frames();
+hipError_t launch_conv0(DType t, const float* pcm, const int32_t* valid, int32_t L, int32_t B,
+                        const float* w0, const float* bias, int32_t C, int32_t k, int32_t stride,
+                        int32_t T0, void* y, float2* stats, const float* gamma, const float* beta,
+                        float eps, hipStream_t s);
+// GroupNorm finalize: chunk partials -> per (b, c) scale = gamma*rstd and
+// shift = beta - mean*gamma*rstd.
+hipError_t launch_gn_finalize(const float2* stats, int32_t B, int32_t C, int32_t T0, int32_t chunk,
+                              const float* gamma, const float* beta, float eps, float2* scale_shift,
+                              hipStream_t s);
+// y = GELU(y * scale[b, c] + shift[b, c]) in place on [B, T, C].
+hipError_t launch_gn_apply_gelu(DType t, void* y, const float2* scale_shift, int32_t B, int32_t T,
+                                int32_t C, hipStream_t s);
+
+// ----------------------------------------------------------------------------
+// row kernels
+// ----------------------------------------------------------------------------
+// LayerNorm over the C entries of each of R rows.  Input fp32 (x_f32) or the
+// operand type (x_t); outputs fp32 (y_f32) and/or operand type (y_t); act 1
+// applies exact GELU after the affine map.  Input and output may alias.
+hipError_t launch_layernorm(DType t, const float* x_f32, const void* x_t, int64_t R, int32_t C,
+                            const float* gamma, const float* beta, float eps, float* y_f32,
+                            void* y_t, int32_t act, hipStream_t s);
+// Positional-conv input: h fp32 [B, T, d] -> zg [G][B][T + K][d/G] (operand
+// type) with `pad` zero frames before the data and zeros after it.
+hipError_t launch_pos_pack(DType t, const float* h, int32_t B, int32_t T, int32_t d, int32_t G,
+                           int32_t Kp, int32_t pad, void* zg, hipStream_t s);
+// dtype conversions [n]
+hipError_t launch_cast_to_f32(DType t, const void* x, float* y, int64_t n, hipStream_t s);
+hipError_t launch_cast_from_f32(DType t, const float* x, void* y, int64_t n, hipStream_t s);
+// frames per row from valid samples (conv length rule)
+hipError_t launch_valid_frames(const int32_t* valid, int32_t B, int32_t window, int32_t n_conv,
+                               const int32_t* kernel, const int32_t* stride, int32_t* vframes,
+                               hipStream_t s);
+
+// ----------------------------------------------------------------------------
+// attention: qkv [B*T, 3d] (q | k | v, head h at columns h*dh), out [B*T, d]
+// ----------------------------------------------------------------------------
+bool attention_supported(int dh);
+hipError_t launch_attention(DType t, const void* qkv, void* out, int32_t B, int32_t T, int32_t H,
+                            int32_t dh, hipStream_t s);
+
+// ----------------------------------------------------------------------------
+// CTC
+// ----------------------------------------------------------------------------
+hipError_t launch_frame_argmax(const float* logits, int64_t rows, int32_t V, int32_t* out,
+                               hipStream_t s);
+hipError_t launch_ctc_collapse(const int32_t* vframes, int32_t B, int32_t T, int32_t blank,
+                               int32_t* ids, int32_t* lens, hipStream_t s);
+
+}  // namespace w2v2

@@ -1,0 +1,839 @@
+// Runtime and C ABI of the wav2vec2-CTC inference library.
+//
+// w2v2_create validates the configuration and the weight table, folds the
+// positional-conv weight norm (w = g * v / ||v|| per tap, in double), casts
+// the weights to the operand type, repacks them into the layouts the
+// kernels read (conv kernels as [C_out, k*C_in] GEMM rows, fused QKV, the
+// positional conv split per group) and uploads them as one allocation.  The
+// workspace for max_batch windows is allocated once; the forward calls only
+// enqueue kernels on the caller's stream.
+//
+// Data layout in device memory (channels-last throughout):
+//   conv i output        [B, T_i, C_i]   operand type, ping-pong buffers A/B
+//   GroupNorm partials   [B, chunks, C_0] (mean, M2) fp32
+//   residual stream h    [B*T, d]        fp32
+//   GEMM operand x       [B*T, max(d, C_last)]  operand type (LayerNorm output)
+//   qkv                  [B*T, 3d]       operand type
+//   attention out        [B*T, d]        operand type
+//   FFN hidden           [B*T, ffn]      operand type
+//   pos-conv input       [G][B][T + K][d/G] operand type, zero padded
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/w2v2.h"
+#include "common.h"
+
+using namespace w2v2;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+w2v2_status fail(w2v2_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+int conv_len(int64_t n, int k, int s) { return n < k ? 0 : (int)((n - k) / s + 1); }
+
+struct ExpectedW {
+  std::string name;
+  std::vector<int64_t> shape;
+};
+
+std::vector<ExpectedW> expected_weights(const w2v2_config& c) {
+  std::vector<ExpectedW> out;
+  int64_t cin = 1;
+  for (int i = 0; i < c.n_conv; ++i) {
+    const int64_t ci = c.conv_dim[i];
+    out.push_back({"fe.conv" + std::to_string(i) + ".weight", {ci, cin, c.conv_kernel[i]}});
+    if (c.conv_bias) out.push_back({"fe.conv" + std::to_string(i) + ".bias", {ci}});
+    if (c.feat_norm == W2V2_NORM_LAYER || i == 0) {
+      out.push_back({"fe.norm" + std::to_string(i) + ".weight", {ci}});
+      out.push_back({"fe.norm" + std::to_string(i) + ".bias", {ci}});
+    }
+    cin = ci;
+  }
+  const int64_t d = c.hidden, cl = c.conv_dim[c.n_conv - 1];
+  out.push_back({"fp.norm.weight", {cl}});
+  out.push_back({"fp.norm.bias", {cl}});
+  out.push_back({"fp.proj.weight", {d, cl}});
+  out.push_back({"fp.proj.bias", {d}});
+  out.push_back({"pos.weight_v", {d, d / c.pos_groups, c.pos_kernel}});
+  out.push_back({"pos.weight_g", {c.pos_kernel}});
+  out.push_back({"pos.bias", {d}});
+  out.push_back({"enc.norm.weight", {d}});
+  out.push_back({"enc.norm.bias", {d}});
+  for (int l = 0; l < c.layers; ++l) {
+    const std::string p = "layer" + std::to_string(l) + ".";
+    for (const char* pr : {"q", "k", "v", "out"}) {
+      out.push_back({p + "attn." + pr + ".weight", {d, d}});
+      out.push_back({p + "attn." + pr + ".bias", {d}});
+    }
+    out.push_back({p + "attn_norm.weight", {d}});
+    out.push_back({p + "attn_norm.bias", {d}});
+    out.push_back({p + "ffn.fc1.weight", {c.ffn, d}});
+    out.push_back({p + "ffn.fc1.bias", {c.ffn}});
+    out.push_back({p + "ffn.fc2.weight", {d, c.ffn}});
+    out.push_back({p + "ffn.fc2.bias", {d}});
+    out.push_back({p + "ffn_norm.weight", {d}});
+    out.push_back({p + "ffn_norm.bias", {d}});
+  }
+  out.push_back({"head.weight", {c.vocab, d}});
+  out.push_back({"head.bias", {c.vocab}});
+  return out;
+}
+
+std::string check_config(const w2v2_config& c, int* frames_out) {
+  auto bad = [](const char* m) { return std::string(m); };
+  if (c.abi_version != W2V2_ABI_VERSION) return bad("abi_version does not match W2V2_ABI_VERSION");
+  if (c.n_conv < 1 || c.n_conv > W2V2_MAX_CONV) return bad("n_conv must be in [1, 8]");
+  for (int i = 0; i < c.n_conv; ++i) {
+    if (c.conv_dim[i] < 8 || c.conv_dim[i] > 2048 || c.conv_dim[i] % 8)
+      return bad("conv_dim must be a multiple of 8 in [8, 2048]");
+    if (c.conv_kernel[i] < 1 || c.conv_stride[i] < 1) return bad("conv kernel and stride must be >= 1");
+  }
+  if (c.conv_dim[0] > 512) return bad("conv_dim[0] must be <= 512");
+  if (c.conv_kernel[0] > 16) return bad("conv_kernel[0] must be <= 16");
+  if (c.conv_stride[0] > 64) return bad("conv_stride[0] must be <= 64");
+  if (c.conv_bias != 0 && c.conv_bias != 1) return bad("conv_bias must be 0 or 1");
+  if (c.feat_norm != W2V2_NORM_GROUP && c.feat_norm != W2V2_NORM_LAYER) return bad("unknown feat_norm");
+  if (c.hidden < 8 || c.hidden > 2048 || c.hidden % 8) return bad("hidden must be a multiple of 8 in [8, 2048]");
+  if (c.heads < 1 || c.hidden % c.heads) return bad("hidden must be divisible by heads");
+  if (!attention_supported(c.hidden / c.heads)) return bad("head size hidden/heads must be 16, 32, 64 or 128");
+  if (c.ffn < 8 || c.ffn % 8) return bad("ffn must be a positive multiple of 8");
+  if (c.layers < 0) return bad("layers must be >= 0");
+  if (c.pos_kernel < 1 || c.pos_groups < 1) return bad("pos_kernel and pos_groups must be >= 1");
+  if (c.hidden % c.pos_groups || (c.hidden / c.pos_groups) % 8)
+    return bad("hidden / pos_groups must be a multiple of 8");
+  if (c.stable_layer_norm != 0 && c.stable_layer_norm != 1) return bad("stable_layer_norm must be 0 or 1");
+  if (c.vocab < 1) return bad("vocab must be >= 1");
+  if (c.blank_id < 0 || c.blank_id >= c.vocab) return bad("blank_id must be in [0, vocab)");
+  if (!(c.eps > 0.f) || !std::isfinite(c.eps)) return bad("eps must be positive and finite");
+  if (c.precision != W2V2_FP32 && c.precision != W2V2_FP16) return bad("unknown precision");
+  if (c.max_batch < 1 || c.max_batch > 4096) return bad("max_batch must be in [1, 4096]");
+  if (c.window < 1) return bad("window must be >= 1");
+  int64_t n = c.window;
+  for (int i = 0; i < c.n_conv; ++i) n = conv_len(n, c.conv_kernel[i], c.conv_stride[i]);
+  if (n < 1) return bad("window is shorter than the feature encoder's receptive field");
+  if (n > 16384) return bad("at most 16384 frames per window are supported");
+  const int64_t t0 = conv_len(c.window, c.conv_kernel[0], c.conv_stride[0]);
+  if ((int64_t)c.max_batch * t0 > (int64_t)INT32_MAX / 2) return bad("max_batch * frames of conv 0 too large");
+  *frames_out = (int)n;
+  return "";
+}
+
+// ----------------------------------------------------------------------------
+// kernel timing
+// ----------------------------------------------------------------------------
+struct Profiler : LaunchHook {
+  struct Rec {
+    const char* name;
+    hipEvent_t a, b;
+  };
+  std::vector<hipEvent_t> pool;
+  std::vector<Rec> recs;
+  std::map<std::string, std::pair<double, int64_t>> totals;
+  std::map<std::string, const char*> names;  // stable name strings
+  hipEvent_t pending = nullptr;
+  hipError_t err = hipSuccess;
+
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) err = r;
+    return e;
+  }
+  void before(const char*, hipStream_t s) override {
+    pending = get();
+    if (pending) {
+      hipError_t r = hipEventRecord(pending, s);
+      if (r != hipSuccess) err = r;
+    }
+  }
+  void after(const char* name, hipStream_t s) override {
+    hipEvent_t e = get();
+    if (e) {
+      hipError_t r = hipEventRecord(e, s);
+      if (r != hipSuccess) err = r;
+    }
+    if (pending && e) recs.push_back({name, pending, e});
+    pending = nullptr;
+  }
+  ~Profiler() override {
+    for (auto& r : recs) {
+      (void)hipEventDestroy(r.a);
+      (void)hipEventDestroy(r.b);
+    }
+    for (auto e : pool) (void)hipEventDestroy(e);
+  }
+};
+
+}  // namespace
+
+// ----------------------------------------------------------------------------
+// model
+// ----------------------------------------------------------------------------
+struct w2v2_model {
+  w2v2_config cfg{};
+  int device = 0;
+  DType dt = DType::F16;
+  int T[W2V2_MAX_CONV] = {};  // frames after conv i
+  int Tf = 0;                 // frames per window
+  int nchunk0 = 0;
+
+  void* wmem = nullptr;
+  size_t wbytes = 0;
+  void* ws = nullptr;
+  size_t wsbytes = 0;
+
+  // weights (device)
+  struct Conv {
+    const void* w = nullptr;      // i = 0: fp32 [C][k]; i > 0: operand type [C_out][k*C_in]
+    const float* bias = nullptr;  // fp32 [C] or null
+    const float* gamma = nullptr;
+    const float* beta = nullptr;
+  } conv[W2V2_MAX_CONV];
+  const float *fp_g = nullptr, *fp_b = nullptr, *fp_bias = nullptr;
+  const void* fp_w = nullptr;
+  const void* pos_w = nullptr;  // [G][Cg][K*Cg]
+  const float* pos_bias = nullptr;
+  const float *enc_g = nullptr, *enc_b = nullptr;
+  struct Layer {
+    const void *wqkv = nullptr, *wo = nullptr, *w1 = nullptr, *w2 = nullptr;
+    const float *bqkv = nullptr, *bo = nullptr, *b1 = nullptr, *b2 = nullptr;
+    const float *ln1_g = nullptr, *ln1_b = nullptr, *ln2_g = nullptr, *ln2_b = nullptr;
+  };
+  std::vector<Layer> layers;
+  const void* head_w = nullptr;
+  const float* head_b = nullptr;
+
+  // workspace regions
+  void *bufA = nullptr, *bufB = nullptr;
+  float2 *gn_stats = nullptr, *gn_ss = nullptr;
+  float* h = nullptr;
+  void *x = nullptr, *qkv = nullptr, *attn = nullptr, *ffn = nullptr, *zg = nullptr;
+
+  Profiler* prof = nullptr;
+  bool prof_on = false;
+
+  ~w2v2_model() {
+    delete prof;
+    if (wmem) (void)hipFree(wmem);
+    if (ws) (void)hipFree(ws);
+  }
+};
+
+namespace {
+
+struct Arena {
+  std::vector<uint8_t> bytes;
+  size_t add(const void* src, size_t n) {
+    size_t off = (bytes.size() + 255) & ~size_t(255);
+    bytes.resize(off + n);
+    memcpy(bytes.data() + off, src, n);
+    return off;
+  }
+};
+
+size_t add_f32(Arena& a, const std::vector<float>& v) { return a.add(v.data(), v.size() * 4); }
+
+size_t add_t(Arena& a, DType dt, const std::vector<float>& v) {
+  if (dt == DType::F32) return add_f32(a, v);
+  std::vector<_Float16> h(v.size());
+  for (size_t i = 0; i < v.size(); ++i) h[i] = (_Float16)v[i];
+  return a.add(h.data(), h.size() * 2);
+}
+
+#define W2V2_LAUNCH(m, s, name, call)                                                 \
+  do {                                                                                \
+    if ((m)->prof_on) (m)->prof->before(name, s);                                     \
+    hipError_t e_ = (call);                                                           \
+    if ((m)->prof_on) (m)->prof->after(name, s);                                      \
+    if (e_ != hipSuccess)                                                             \
+      return fail(W2V2_E_DEVICE, std::string(name) + ": " + hipGetErrorString(e_));  \
+  } while (0)
+
+// conv 0 .. n-1; returns the final conv output buffer in *feat
+w2v2_status run_frontend(w2v2_model* m, const float* pcm, const int32_t* valid, int B, hipStream_t s,
+                         const void** feat) {
+  const w2v2_config& c = m->cfg;
+  const DType dt = m->dt;
+  const int C0 = c.conv_dim[0];
+  if (c.feat_norm == W2V2_NORM_GROUP) {
+    W2V2_LAUNCH(m, s, "conv0_gn_stats",
+                launch_conv0(dt, pcm, valid, c.window, B, (const float*)m->conv[0].w, m->conv[0].bias, C0,
+                             c.conv_kernel[0], c.conv_stride[0], m->T[0], m->bufA, m->gn_stats, nullptr, nullptr,
+                             c.eps, s));
+    W2V2_LAUNCH(m, s, "gn_finalize",
+                launch_gn_finalize(m->gn_stats, B, C0, m->T[0], conv0_chunk_frames(), m->conv[0].gamma,
+                                   m->conv[0].beta, c.eps, m->gn_ss, s));
+    W2V2_LAUNCH(m, s, "gn_apply_gelu", launch_gn_apply_gelu(dt, m->bufA, m->gn_ss, B, m->T[0], C0, s));
+  } else {
+    W2V2_LAUNCH(m, s, "conv0_ln_gelu",
+                launch_conv0(dt, pcm, valid, c.window, B, (const float*)m->conv[0].w, m->conv[0].bias, C0,
+                             c.conv_kernel[0], c.conv_stride[0], m->T[0], m->bufA, nullptr, m->conv[0].gamma,
+                             m->conv[0].beta, c.eps, s));
+  }
+  const void* cur = m->bufA;
+  int tin = m->T[0], cin = C0;
+  for (int i = 1; i < c.n_conv; ++i) {
+    void* out = (i & 1) ? m->bufB : m->bufA;
+    GemmArgs g;
+    g.A = cur;
+    g.lda = (int64_t)c.conv_stride[i] * cin;
+    g.a_seg = (int64_t)tin * cin;
+    g.seg_rows = m->T[i];
+    g.B = m->conv[i].w;
+    g.M = B * m->T[i];
+    g.N = c.conv_dim[i];
+    g.K = c.conv_kernel[i] * cin;
+    g.bias = m->conv[i].bias;
+    g.out_t = out;
+    g.ldc = c.conv_dim[i];
+    g.act = (c.feat_norm == W2V2_NORM_GROUP) ? 1 : 0;
+    W2V2_LAUNCH(m, s, "conv_gemm", launch_gemm(dt, g, s));
+    if (c.feat_norm == W2V2_NORM_LAYER) {
+      W2V2_LAUNCH(m, s, "conv_ln_gelu",
+                  launch_layernorm(dt, nullptr, out, (int64_t)B * m->T[i], c.conv_dim[i], m->conv[i].gamma,
+                                   m->conv[i].beta, c.eps, nullptr, out, 1, s));
+    }
+    cur = out;
+    tin = m->T[i];
+    cin = c.conv_dim[i];
+  }
+  *feat = cur;
+  return W2V2_OK;
+}
+
+w2v2_status gemm_linear(w2v2_model* m, hipStream_t s, const char* name, const void* A, int M, int N, int K,
+                        const void* W, const float* bias, int act, const float* residual, float* out32,
+                        void* outt, int64_t ldc) {
+  GemmArgs g;
+  g.A = A;
+  g.lda = K;
+  g.a_seg = 0;
+  g.seg_rows = M;
+  g.B = W;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.bias = bias;
+  g.act = act;
+  g.residual = residual;
+  g.out_f32 = out32;
+  g.out_t = outt;
+  g.ldc = ldc;
+  W2V2_LAUNCH(m, s, name, launch_gemm(m->dt, g, s));
+  return W2V2_OK;
+}
+
+#define W2V2_TRY(call)                  \
+  do {                                  \
+    w2v2_status st_ = (call);           \
+    if (st_ != W2V2_OK) return st_;     \
+  } while (0)
+
+w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, hipStream_t s) {
+  const w2v2_config& c = m->cfg;
+  const DType dt = m->dt;
+  const int T = m->Tf, d = c.hidden, F = c.ffn, G = c.pos_groups, Cg = d / G, K = c.pos_kernel;
+  const int cl = c.conv_dim[c.n_conv - 1];
+  const int M = B * T;
+  const float eps = c.eps;
+
+  // feature projection: LN over channels, then Linear C -> d (fp32 residual stream)
+  W2V2_LAUNCH(m, s, "layernorm",
+              launch_layernorm(dt, nullptr, feat, M, cl, m->fp_g, m->fp_b, eps, nullptr, m->x, 0, s));
+  W2V2_TRY(gemm_linear(m, s, "gemm_feature_proj", m->x, M, d, cl, m->fp_w, m->fp_bias, 0, nullptr, m->h, nullptr, d));
+
+  // positional conv: h = z + GELU(posconv(z) + bias)
+  const int pad = K / 2;
+  W2V2_LAUNCH(m, s, "pos_pack", launch_pos_pack(dt, m->h, B, T, d, G, K, pad, m->zg, s));
+  {
+    GemmArgs g;
+    g.A = m->zg;
+    g.lda = Cg;
+    g.a_seg = (int64_t)(T + K) * Cg;
+    g.seg_rows = T;
+    g.a_group = (int64_t)B * (T + K) * Cg;
+    g.B = m->pos_w;
+    g.b_group = (int64_t)Cg * K * Cg;
+    g.M = M;
+    g.N = Cg;
+    g.K = K * Cg;
+    g.groups = G;
+    g.bias = m->pos_bias;
+    g.bias_group = Cg;
+    g.act = 1;
+    g.residual = m->h;
+    g.out_f32 = m->h;
+    g.ldc = d;
+    g.c_group = Cg;
+    W2V2_LAUNCH(m, s, "pos_conv_gemm", launch_gemm(dt, g, s));
+  }
+  const bool stable = c.stable_layer_norm != 0;
+  if (!stable)
+    W2V2_LAUNCH(m, s, "layernorm",
+                launch_layernorm(dt, m->h, nullptr, M, d, m->enc_g, m->enc_b, eps, m->h, m->x, 0, s));
+
+  for (int l = 0; l < c.layers; ++l) {
+    const w2v2_model::Layer& L = m->layers[l];
+    if (stable)
+      W2V2_LAUNCH(m, s, "layernorm",
+                  launch_layernorm(dt, m->h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, nullptr, m->x, 0, s));
+    W2V2_TRY(gemm_linear(m, s, "gemm_qkv", m->x, M, 3 * d, d, L.wqkv, L.bqkv, 0, nullptr, nullptr, m->qkv, 3 * d));
+    W2V2_LAUNCH(m, s, "attention", launch_attention(dt, m->qkv, m->attn, B, T, c.heads, d / c.heads, s));
+    W2V2_TRY(gemm_linear(m, s, "gemm_out_proj", m->attn, M, d, d, L.wo, L.bo, 0, m->h, m->h, nullptr, d));
+    if (stable)
+      W2V2_LAUNCH(m, s, "layernorm",
+                  launch_layernorm(dt, m->h, nullptr, M, d, L.ln2_g, L.ln2_b, eps, nullptr, m->x, 0, s));
+    else
+      W2V2_LAUNCH(m, s, "layernorm",
+                  launch_layernorm(dt, m->h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, m->h, m->x, 0, s));
+    W2V2_TRY(gemm_linear(m, s, "gemm_ffn1", m->x, M, F, d, L.w1, L.b1, 1, nullptr, nullptr, m->ffn, F));
+    W2V2_TRY(gemm_linear(m, s, "gemm_ffn2", m->ffn, M, d, F, L.w2, L.b2, 0, m->h, m->h, nullptr, d));
+    if (!stable)
+      W2V2_LAUNCH(m, s, "layernorm",
+                  launch_layernorm(dt, m->h, nullptr, M, d, L.ln2_g, L.ln2_b, eps, m->h, m->x, 0, s));
+  }
+  if (stable)
+    W2V2_LAUNCH(m, s, "layernorm",
+                launch_layernorm(dt, m->h, nullptr, M, d, m->enc_g, m->enc_b, eps, nullptr, m->x, 0, s));
+  W2V2_TRY(gemm_linear(m, s, "gemm_ctc_head", m->x, M, c.vocab, d, m->head_w, m->head_b, 0, nullptr, logits,
+                       nullptr, c.vocab));
+  return W2V2_OK;
+}
+
+w2v2_status check_forward_args(w2v2_model* m, const void* a, const void* b, int32_t batch, const void* c) {
+  if (!m) return fail(W2V2_E_ARG, "model is NULL");
+  if (!a || !b || !c) return fail(W2V2_E_ARG, "a required device pointer is NULL");
+  if (batch < 1 || batch > m->cfg.max_batch)
+    return fail(W2V2_E_ARG, "batch must be in [1, max_batch=" + std::to_string(m->cfg.max_batch) + "]");
+  return W2V2_OK;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------
+// C ABI
+// ----------------------------------------------------------------------------
+extern "C" {
+
+const char* w2v2_last_error(void) { return g_last_error.c_str(); }
+
+w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int32_t n_weights, int32_t device,
+                        w2v2_model** out) {
+  g_last_error.clear();
+  if (!out) return fail(W2V2_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (!cfgp) return fail(W2V2_E_ARG, "cfg is NULL");
+  if (n_weights < 0) return fail(W2V2_E_ARG, "n_weights < 0");
+  const w2v2_config c = *cfgp;
+  int frames = 0;
+  const std::string cerr = check_config(c, &frames);
+  if (!cerr.empty()) return fail(W2V2_E_CONFIG, cerr);
+
+  // ---- weight table ----
+  if (n_weights == 0 || !weights) return fail(W2V2_E_WEIGHTS, "weight table is empty");
+  const std::vector<ExpectedW> exp = expected_weights(c);
+  std::map<std::string, const w2v2_tensor*> got;
+  for (int i = 0; i < n_weights; ++i) {
+    const w2v2_tensor& t = weights[i];
+    if (!t.name) return fail(W2V2_E_WEIGHTS, "weight " + std::to_string(i) + " has no name");
+    if (got.count(t.name)) return fail(W2V2_E_WEIGHTS, std::string("duplicate weight ") + t.name);
+    got[t.name] = &t;
+  }
+  for (const auto& e : exp) {
+    auto it = got.find(e.name);
+    if (it == got.end()) return fail(W2V2_E_WEIGHTS, "missing weight " + e.name);
+    const w2v2_tensor& t = *it->second;
+    if (!t.data) return fail(W2V2_E_WEIGHTS, "weight " + e.name + " has no data");
+    if (t.ndim < 1 || t.ndim > 4) return fail(W2V2_E_WEIGHTS, "weight " + e.name + " has bad ndim");
+    std::vector<int64_t> sh(t.shape, t.shape + t.ndim);
+    bool ok = (sh == e.shape);
+    if (!ok && e.name == "pos.weight_g" && sh.size() == 3 && sh[0] == 1 && sh[1] == 1 && sh[2] == e.shape[0])
+      ok = true;
+    if (!ok) return fail(W2V2_E_WEIGHTS, "weight " + e.name + " has the wrong shape");
+    int64_t n = 1;
+    for (auto v : e.shape) n *= v;
+    for (int64_t j = 0; j < n; ++j)
+      if (!std::isfinite(t.data[j])) return fail(W2V2_E_WEIGHTS, "weight " + e.name + " has a non-finite value");
+  }
+  if ((size_t)n_weights != exp.size()) {
+    for (const auto& kv : got) {
+      bool known = false;
+      for (const auto& e : exp) known = known || (e.name == kv.first);
+      if (!known) return fail(W2V2_E_WEIGHTS, "unknown weight " + kv.first);
+    }
+    return fail(W2V2_E_WEIGHTS, "weight table has the wrong number of entries");
+  }
+  auto W = [&](const std::string& n) { return got[n]->data; };
+  auto Wv = [&](const std::string& n, size_t count) {
+    const float* p = W(n);
+    return std::vector<float>(p, p + count);
+  };
+
+  // ---- device ----
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return fail(W2V2_E_DEVICE, "no HIP device");
+  if (device < 0 || device >= ndev) return fail(W2V2_E_DEVICE, "device index out of range");
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return fail(W2V2_E_DEVICE, "hipGetDeviceProperties failed");
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(W2V2_E_DEVICE, std::string("device is ") + prop.gcnArchName + ", this library is built for gfx950");
+  DeviceGuard guard(device);
+
+  w2v2_model* m = new w2v2_model();
+  m->cfg = c;
+  m->device = device;
+  m->dt = c.precision == W2V2_FP16 ? DType::F16 : DType::F32;
+  {
+    int64_t n = c.window;
+    for (int i = 0; i < c.n_conv; ++i) {
+      n = conv_len(n, c.conv_kernel[i], c.conv_stride[i]);
+      m->T[i] = (int)n;
+    }
+    m->Tf = frames;
+    m->nchunk0 = (m->T[0] + conv0_chunk_frames() - 1) / conv0_chunk_frames();
+  }
+  const DType dt = m->dt;
+  const int d = c.hidden, F = c.ffn, G = c.pos_groups, Cg = d / G, K = c.pos_kernel;
+  const int cl = c.conv_dim[c.n_conv - 1];
+
+  // ---- pack weights ----
+  Arena ar;
+  struct Off {
+    size_t w = 0, b = 0, g = 0, be = 0;
+    bool hb = false, hn = false;
+  };
+  std::vector<Off> conv_off(c.n_conv);
+  int cin = 1;
+  for (int i = 0; i < c.n_conv; ++i) {
+    const int co = c.conv_dim[i], k = c.conv_kernel[i];
+    const std::string p = "fe.conv" + std::to_string(i);
+    const float* w = W(p + ".weight");
+    if (i == 0) {
+      conv_off[i].w = add_f32(ar, std::vector<float>(w, w + (size_t)co * k));
+    } else {
+      std::vector<float> r((size_t)co * k * cin);
+      for (int o = 0; o < co; ++o)
+        for (int ci = 0; ci < cin; ++ci)
+          for (int j = 0; j < k; ++j) r[((size_t)o * k + j) * cin + ci] = w[((size_t)o * cin + ci) * k + j];
+      conv_off[i].w = add_t(ar, dt, r);
+    }
+    if (c.conv_bias) {
+      conv_off[i].b = add_f32(ar, Wv(p + ".bias", co));
+      conv_off[i].hb = true;
+    }
+    if (c.feat_norm == W2V2_NORM_LAYER || i == 0) {
+      const std::string n = "fe.norm" + std::to_string(i);
+      conv_off[i].g = add_f32(ar, Wv(n + ".weight", co));
+      conv_off[i].be = add_f32(ar, Wv(n + ".bias", co));
+      conv_off[i].hn = true;
+    }
+    cin = co;
+  }
+  const size_t o_fpg = add_f32(ar, Wv("fp.norm.weight", cl));
+  const size_t o_fpb = add_f32(ar, Wv("fp.norm.bias", cl));
+  const size_t o_fpw = add_t(ar, dt, Wv("fp.proj.weight", (size_t)d * cl));
+  const size_t o_fpbias = add_f32(ar, Wv("fp.proj.bias", d));
+  size_t o_posw, o_posb;
+  {
+    // weight norm folded per tap: w[o, i, k] = g[k] v[o, i, k] / ||v[:, :, k]||_F
+    const float* v = W("pos.weight_v");
+    const float* gk = W("pos.weight_g");
+    std::vector<double> scale(K);
+    for (int k = 0; k < K; ++k) {
+      double ss = 0.0;
+      for (int o = 0; o < d; ++o)
+        for (int i = 0; i < Cg; ++i) {
+          const double x = v[((size_t)o * Cg + i) * K + k];
+          ss += x * x;
+        }
+      scale[k] = ss > 0.0 ? (double)gk[k] / std::sqrt(ss) : 0.0;
+    }
+    // [G][Cg_out][K*Cg_in], K index = k*Cg + i
+    std::vector<float> r((size_t)d * K * Cg);
+    for (int g = 0; g < G; ++g)
+      for (int ol = 0; ol < Cg; ++ol) {
+        const int o = g * Cg + ol;
+        for (int k = 0; k < K; ++k)
+          for (int i = 0; i < Cg; ++i)
+            r[(((size_t)g * Cg + ol) * K + k) * Cg + i] = (float)(v[((size_t)o * Cg + i) * K + k] * scale[k]);
+      }
+    o_posw = add_t(ar, dt, r);
+    o_posb = add_f32(ar, Wv("pos.bias", d));
+  }
+  const size_t o_encg = add_f32(ar, Wv("enc.norm.weight", d));
+  const size_t o_encb = add_f32(ar, Wv("enc.norm.bias", d));
+  struct LOff {
+    size_t wqkv, wo, w1, w2, bqkv, bo, b1, b2, g1, be1, g2, be2;
+  };
+  std::vector<LOff> loff(c.layers);
+  for (int l = 0; l < c.layers; ++l) {
+    const std::string p = "layer" + std::to_string(l) + ".";
+    std::vector<float> qkv((size_t)3 * d * d), bq((size_t)3 * d);
+    const char* pr[3] = {"q", "k", "v"};
+    for (int j = 0; j < 3; ++j) {
+      memcpy(qkv.data() + (size_t)j * d * d, W(p + "attn." + pr[j] + ".weight"), sizeof(float) * d * d);
+      memcpy(bq.data() + (size_t)j * d, W(p + "attn." + pr[j] + ".bias"), sizeof(float) * d);
+    }
+    loff[l].wqkv = add_t(ar, dt, qkv);
+    loff[l].bqkv = add_f32(ar, bq);
+    loff[l].wo = add_t(ar, dt, Wv(p + "attn.out.weight", (size_t)d * d));
+    loff[l].bo = add_f32(ar, Wv(p + "attn.out.bias", d));
+    loff[l].g1 = add_f32(ar, Wv(p + "attn_norm.weight", d));
+    loff[l].be1 = add_f32(ar, Wv(p + "attn_norm.bias", d));
+    loff[l].w1 = add_t(ar, dt, Wv(p + "ffn.fc1.weight", (size_t)F * d));
+    loff[l].b1 = add_f32(ar, Wv(p + "ffn.fc1.bias", F));
+    loff[l].w2 = add_t(ar, dt, Wv(p + "ffn.fc2.weight", (size_t)d * F));
+    loff[l].b2 = add_f32(ar, Wv(p + "ffn.fc2.bias", d));
+    loff[l].g2 = add_f32(ar, Wv(p + "ffn_norm.weight", d));
+    loff[l].be2 = add_f32(ar, Wv(p + "ffn_norm.bias", d));
+  }
+  const size_t o_hw = add_t(ar, dt, Wv("head.weight", (size_t)c.vocab * d));
+  const size_t o_hb = add_f32(ar, Wv("head.bias", c.vocab));
+
+  m->wbytes = ar.bytes.size();
+  if (hipMalloc(&m->wmem, m->wbytes) != hipSuccess) {
+    (void)hipGetLastError();
+    delete m;
+    return fail(W2V2_E_NOMEM, "cannot allocate " + std::to_string(ar.bytes.size()) + " bytes of weights");
+  }
+  if (hipMemcpy(m->wmem, ar.bytes.data(), m->wbytes, hipMemcpyHostToDevice) != hipSuccess) {
+    delete m;
+    return fail(W2V2_E_DEVICE, "weight upload failed");
+  }
+  auto P = [&](size_t off) { return (const void*)((const uint8_t*)m->wmem + off); };
+  auto PF = [&](size_t off) { return (const float*)P(off); };
+  for (int i = 0; i < c.n_conv; ++i) {
+    m->conv[i].w = P(conv_off[i].w);
+    m->conv[i].bias = conv_off[i].hb ? PF(conv_off[i].b) : nullptr;
+    m->conv[i].gamma = conv_off[i].hn ? PF(conv_off[i].g) : nullptr;
+    m->conv[i].beta = conv_off[i].hn ? PF(conv_off[i].be) : nullptr;
+  }
+  m->fp_g = PF(o_fpg);
+  m->fp_b = PF(o_fpb);
+  m->fp_w = P(o_fpw);
+  m->fp_bias = PF(o_fpbias);
+  m->pos_w = P(o_posw);
+  m->pos_bias = PF(o_posb);
+  m->enc_g = PF(o_encg);
+  m->enc_b = PF(o_encb);
+  m->layers.resize(c.layers);
+  for (int l = 0; l < c.layers; ++l) {
+    auto& L = m->layers[l];
+    L.wqkv = P(loff[l].wqkv);
+    L.bqkv = PF(loff[l].bqkv);
+    L.wo = P(loff[l].wo);
+    L.bo = PF(loff[l].bo);
+    L.w1 = P(loff[l].w1);
+    L.b1 = PF(loff[l].b1);
+    L.w2 = P(loff[l].w2);
+    L.b2 = PF(loff[l].b2);
+    L.ln1_g = PF(loff[l].g1);
+    L.ln1_b = PF(loff[l].be1);
+    L.ln2_g = PF(loff[l].g2);
+    L.ln2_b = PF(loff[l].be2);
+  }
+  m->head_w = P(o_hw);
+  m->head_b = PF(o_hb);
+
+  // ---- workspace ----
+  const int64_t Bm = c.max_batch;
+  const size_t ds = dsize(dt);
+  int64_t elA = 0, elB = 0;
+  for (int i = 0; i < c.n_conv; ++i) {
+    const int64_t e = Bm * m->T[i] * c.conv_dim[i];
+    if (i & 1) elB = std::max(elB, e);
+    else elA = std::max(elA, e);
+  }
+  const int64_t M = Bm * m->Tf;
+  elA = std::max(elA, M * cl);  // w2v2_forward_encoder stages its input features here
+  std::vector<size_t> sizes = {
+      (size_t)elA * ds,                                   // bufA
+      (size_t)std::max<int64_t>(elB, 1) * ds,             // bufB
+      (size_t)Bm * m->nchunk0 * c.conv_dim[0] * 8,        // gn_stats
+      (size_t)Bm * c.conv_dim[0] * 8,                     // gn_ss
+      (size_t)M * d * 4,                                  // h
+      (size_t)M * std::max(d, cl) * ds,                   // x
+      (size_t)M * 3 * d * ds,                             // qkv
+      (size_t)M * d * ds,                                 // attn
+      (size_t)M * F * ds,                                 // ffn
+      (size_t)G * Bm * (m->Tf + K) * Cg * ds,             // zg
+  };
+  size_t total = 0;
+  std::vector<size_t> offs;
+  for (size_t sz : sizes) {
+    offs.push_back(total);
+    total += (sz + 255) & ~size_t(255);
+  }
+  m->wsbytes = total;
+  if (hipMalloc(&m->ws, total) != hipSuccess) {
+    (void)hipGetLastError();
+    delete m;
+    return fail(W2V2_E_NOMEM, "cannot allocate " + std::to_string(total) + " bytes of workspace");
+  }
+  uint8_t* wsb = (uint8_t*)m->ws;
+  m->bufA = wsb + offs[0];
+  m->bufB = wsb + offs[1];
+  m->gn_stats = (float2*)(wsb + offs[2]);
+  m->gn_ss = (float2*)(wsb + offs[3]);
+  m->h = (float*)(wsb + offs[4]);
+  m->x = wsb + offs[5];
+  m->qkv = wsb + offs[6];
+  m->attn = wsb + offs[7];
+  m->ffn = wsb + offs[8];
+  m->zg = wsb + offs[9];
+  if (hipDeviceSynchronize() != hipSuccess) {
+    delete m;
+    return fail(W2V2_E_DEVICE, "device synchronization failed after weight upload");
+  }
+  *out = m;
+  return W2V2_OK;
+}
+
+void w2v2_destroy(w2v2_model* m) {
+  if (!m) return;
+  DeviceGuard guard(m->device);
+  delete m;
+}
+
+w2v2_status w2v2_num_frames(const w2v2_model* m, int64_t samples, int32_t* frames) {
+  if (!m || !frames) return fail(W2V2_E_ARG, "NULL argument");
+  if (samples < 0) return fail(W2V2_E_ARG, "samples < 0");
+  int64_t n = samples;
+  for (int i = 0; i < m->cfg.n_conv; ++i) n = conv_len(n, m->cfg.conv_kernel[i], m->cfg.conv_stride[i]);
+  *frames = (int32_t)n;
+  return W2V2_OK;
+}
+
+w2v2_status w2v2_model_info(const w2v2_model* m, int32_t* frames_per_window, int32_t* vocab,
+                            int64_t* workspace_bytes) {
+  if (!m) return fail(W2V2_E_ARG, "model is NULL");
+  if (frames_per_window) *frames_per_window = m->Tf;
+  if (vocab) *vocab = m->cfg.vocab;
+  if (workspace_bytes) *workspace_bytes = (int64_t)m->wsbytes;
+  return W2V2_OK;
+}
+
+w2v2_status w2v2_forward(w2v2_model* m, const float* pcm, const int32_t* valid, int32_t batch, float* logits,
+                         int32_t* vframes, void* stream) {
+  W2V2_TRY(check_forward_args(m, pcm, valid, batch, logits));
+  DeviceGuard guard(m->device);
+  hipStream_t s = (hipStream_t)stream;
+  const void* feat = nullptr;
+  W2V2_TRY(run_frontend(m, pcm, valid, batch, s, &feat));
+  W2V2_TRY(run_encoder(m, feat, batch, logits, s));
+  if (vframes)
+    W2V2_LAUNCH(m, s, "valid_frames",
+                launch_valid_frames(valid, batch, m->cfg.window, m->cfg.n_conv, m->cfg.conv_kernel,
+                                    m->cfg.conv_stride, vframes, s));
+  return W2V2_OK;
+}
+
+w2v2_status w2v2_forward_frontend(w2v2_model* m, const float* pcm, const int32_t* valid, int32_t batch,
+                                  float* features, void* stream) {
+  W2V2_TRY(check_forward_args(m, pcm, valid, batch, features));
+  DeviceGuard guard(m->device);
+  hipStream_t s = (hipStream_t)stream;
+  const void* feat = nullptr;
+  W2V2_TRY(run_frontend(m, pcm, valid, batch, s, &feat));
+  const int64_t n = (int64_t)batch * m->Tf * m->cfg.conv_dim[m->cfg.n_conv - 1];
+  W2V2_LAUNCH(m, s, "cast_to_f32", launch_cast_to_f32(m->dt, feat, features, n, s));
+  return W2V2_OK;
+}
+
+w2v2_status w2v2_forward_encoder(w2v2_model* m, const float* features, int32_t batch, float* logits,
+                                 void* stream) {
+  W2V2_TRY(check_forward_args(m, features, features, batch, logits));
+  DeviceGuard guard(m->device);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t n = (int64_t)batch * m->Tf * m->cfg.conv_dim[m->cfg.n_conv - 1];
+  W2V2_LAUNCH(m, s, "cast_from_f32", launch_cast_from_f32(m->dt, features, m->bufA, n, s));
+  W2V2_TRY(run_encoder(m, m->bufA, batch, logits, s));
+  return W2V2_OK;
+}
+
+w2v2_status w2v2_ctc_greedy(const float* logits, const int32_t* vframes, int32_t batch, int32_t frames,
+                            int32_t vocab, int32_t blank_id, int32_t* ids, int32_t* lens, void* stream) {
+  if (!logits || !vframes || !ids || !lens) return fail(W2V2_E_ARG, "a required device pointer is NULL");
+  if (batch < 1) return fail(W2V2_E_ARG, "batch must be >= 1");
+  if (frames < 1 || frames > 16384) return fail(W2V2_E_ARG, "frames must be in [1, 16384]");
+  if (vocab < 1) return fail(W2V2_E_ARG, "vocab must be >= 1");
+  if (blank_id < 0 || blank_id >= vocab) return fail(W2V2_E_ARG, "blank_id must be in [0, vocab)");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_frame_argmax(logits, (int64_t)batch * frames, vocab, ids, s);
+  if (e == hipSuccess) e = launch_ctc_collapse(vframes, batch, frames, blank_id, ids, lens, s);
+  if (e != hipSuccess) return fail(W2V2_E_DEVICE, std::string("ctc_greedy: ") + hipGetErrorString(e));
+  return W2V2_OK;
+}
+
+w2v2_status w2v2_profile_enable(w2v2_model* m, int32_t enable) {
+  if (!m) return fail(W2V2_E_ARG, "model is NULL");
+  if (enable && !m->prof) m->prof = new Profiler();
+  m->prof_on = enable != 0;
+  return W2V2_OK;
+}
+
+w2v2_status w2v2_profile_read(w2v2_model* m, int32_t cap, const char** names, double* total_ms,
+                              int64_t* launches, int32_t* n) {
+  if (!m || !n || cap < 0 || (cap > 0 && (!names || !total_ms || !launches)))
+    return fail(W2V2_E_ARG, "bad argument");
+  *n = 0;
+  if (!m->prof) return W2V2_OK;
+  DeviceGuard guard(m->device);
+  Profiler& p = *m->prof;
+  if (p.err != hipSuccess) return fail(W2V2_E_DEVICE, std::string("profiling: ") + hipGetErrorString(p.err));
+  for (auto& r : p.recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return fail(W2V2_E_DEVICE, "hipEventSynchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(W2V2_E_DEVICE, "hipEventElapsedTime failed");
+    auto& t = p.totals[r.name];
+    t.first += ms;
+    t.second += 1;
+    if (!p.names.count(r.name)) p.names[r.name] = r.name;
+    p.pool.push_back(r.a);
+    p.pool.push_back(r.b);
+  }
+  p.recs.clear();
+  int i = 0;
+  for (auto& kv : p.totals) {
+    if (i < cap) {
+      names[i] = p.names[kv.first];
+      total_ms[i] = kv.second.first;
+      launches[i] = kv.second.second;
+    }
+    ++i;
+  }
+  *n = i;
+  p.totals.clear();
+  return W2V2_OK;
+}
+
+}  // extern "C"

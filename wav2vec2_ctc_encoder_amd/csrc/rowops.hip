@@ -1,0 +1,193 @@
+// Row-wise and elementwise kernels: LayerNorm (+ optional GELU), the
+// zero-padded per-group packing that feeds the positional conv, and casts.
+//
+// LayerNorm: one wave per row, the row held in registers as float4 groups
+// (lane i takes elements 4i, 4i+256, ...), statistics in fp32 with wave
+// reductions (biased variance, eps inside the square root), two passes over
+// registers for mean then centred variance.  Memory bound: one read of the
+// row and one or two writes (fp32 residual stream and/or the fp16 GEMM
+// operand).
+#include "common.h"
+
+namespace w2v2 {
+namespace {
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+__device__ inline float gelu_exact(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <typename T>
+__device__ inline float4 load4(const T* p);
+template <>
+__device__ inline float4 load4<float>(const float* p) { return *(const float4*)p; }
+template <>
+__device__ inline float4 load4<half_t>(const half_t* p) {
+  const h4 h = *(const h4*)p;
+  return make_float4((float)h.x, (float)h.y, (float)h.z, (float)h.w);
+}
+template <typename T>
+__device__ inline void store4(T* p, float4 v);
+template <>
+__device__ inline void store4<float>(float* p, float4 v) { *(float4*)p = v; }
+template <>
+__device__ inline void store4<half_t>(half_t* p, float4 v) {
+  h4 h = {(half_t)v.x, (half_t)v.y, (half_t)v.z, (half_t)v.w};
+  *(h4*)p = h;
+}
+
+// NV: float4 groups per lane (C <= 256 * NV).  XT: input type.
+// x may alias y32 / yt (in-place use): every lane reads its whole row slice
+// before writing it, so no restrict qualifiers here.
+template <typename T, typename XT, int NV>
+__global__ __launch_bounds__(256) void layernorm_kernel(const XT* x, int64_t R, int C,
+                                                        const float* __restrict__ gamma,
+                                                        const float* __restrict__ beta, float eps,
+                                                        float* y32, T* yt, int act) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= R) return;
+  const XT* xr = x + row * C;
+  float4 v[NV];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = 4 * (lane + 64 * i);
+    if (c < C) {
+      v[i] = load4<XT>(xr + c);
+      s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    } else {
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  const float invC = 1.f / (float)C;
+  const float mean = wave_sum(s) * invC;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = 4 * (lane + 64 * i);
+    if (c < C) {
+      const float a = v[i].x - mean, b = v[i].y - mean, cc = v[i].z - mean, d = v[i].w - mean;
+      q += (a * a + b * b) + (cc * cc + d * d);
+    }
+  }
+  const float rstd = rsqrtf(wave_sum(q) * invC + eps);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = 4 * (lane + 64 * i);
+    if (c < C) {
+      const float4 g = *(const float4*)(gamma + c);
+      const float4 b = *(const float4*)(beta + c);
+      float4 o;
+      o.x = (v[i].x - mean) * rstd * g.x + b.x;
+      o.y = (v[i].y - mean) * rstd * g.y + b.y;
+      o.z = (v[i].z - mean) * rstd * g.z + b.z;
+      o.w = (v[i].w - mean) * rstd * g.w + b.w;
+      if (act == 1) {
+        o.x = gelu_exact(o.x); o.y = gelu_exact(o.y); o.z = gelu_exact(o.z); o.w = gelu_exact(o.w);
+      }
+      if (y32) *(float4*)(y32 + row * C + c) = o;
+      if (yt) store4<T>(yt + row * C + c, o);
+    }
+  }
+}
+
+template <typename T, typename XT>
+hipError_t ln_dispatch(const XT* x, int64_t R, int C, const float* g, const float* b, float eps, float* y32,
+                       T* yt, int act, hipStream_t s) {
+  const dim3 grid((unsigned)((R + 3) / 4)), block(256);
+  const int nv = (C + 255) / 256;
+  if (nv <= 1) hipLaunchKernelGGL((layernorm_kernel<T, XT, 1>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act);
+  else if (nv == 2) hipLaunchKernelGGL((layernorm_kernel<T, XT, 2>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act);
+  else if (nv == 3) hipLaunchKernelGGL((layernorm_kernel<T, XT, 3>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act);
+  else if (nv == 4) hipLaunchKernelGGL((layernorm_kernel<T, XT, 4>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act);
+  else hipLaunchKernelGGL((layernorm_kernel<T, XT, 8>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act);
+  return hipGetLastError();
+}
+
+// zg[g][b][p][i] = h[b, p - pad, g*Cg + i] for 0 <= p - pad < T, else 0.
+template <typename T>
+__global__ __launch_bounds__(256) void pos_pack_kernel(const float* __restrict__ h, int B, int Tn, int d, int G,
+                                                       int Tp, int pad, T* __restrict__ zg, int64_t nvec) {
+  const int Cg = d / G;
+  const int cv = Cg / 4;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec;
+       v += (int64_t)gridDim.x * blockDim.x) {
+    const int i4 = (int)(v % cv);
+    int64_t r = v / cv;
+    const int p = (int)(r % Tp);
+    r /= Tp;
+    const int b = (int)(r % B);
+    const int g = (int)(r / B);
+    const int t = p - pad;
+    float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t >= 0 && t < Tn) val = *(const float4*)(h + ((int64_t)b * Tn + t) * d + g * Cg + 4 * i4);
+    store4<T>(zg + v * 4, val);
+  }
+}
+
+template <typename T>
+__global__ void cast_to_f32_kernel(const T* __restrict__ x, float* __restrict__ y, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    y[i] = (float)x[i];
+}
+template <typename T>
+__global__ void cast_from_f32_kernel(const float* __restrict__ x, T* __restrict__ y, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    y[i] = (T)x[i];
+}
+
+inline int grid_for(int64_t work) {
+  const int64_t g = (work + 255) / 256;
+  return (int)(g < 16384 ? (g < 1 ? 1 : g) : 16384);
+}
+
+}  // namespace
+
+hipError_t launch_layernorm(DType t, const float* x_f32, const void* x_t, int64_t R, int32_t C,
+                            const float* gamma, const float* beta, float eps, float* y_f32, void* y_t,
+                            int32_t act, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  if (t == DType::F16) {
+    if (x_f32) return ln_dispatch<half_t, float>(x_f32, R, C, gamma, beta, eps, y_f32, (half_t*)y_t, act, s);
+    return ln_dispatch<half_t, half_t>((const half_t*)x_t, R, C, gamma, beta, eps, y_f32, (half_t*)y_t, act, s);
+  }
+  if (x_f32) return ln_dispatch<float, float>(x_f32, R, C, gamma, beta, eps, y_f32, (float*)y_t, act, s);
+  return ln_dispatch<float, float>((const float*)x_t, R, C, gamma, beta, eps, y_f32, (float*)y_t, act, s);
+}
+
+hipError_t launch_pos_pack(DType t, const float* h, int32_t B, int32_t T, int32_t d, int32_t G, int32_t Kp,
+                           int32_t pad, void* zg, hipStream_t s) {
+  const int Tp = T + Kp;
+  const int64_t nvec = (int64_t)G * B * Tp * (d / G) / 4;
+  if (t == DType::F16)
+    hipLaunchKernelGGL(pos_pack_kernel<half_t>, dim3(grid_for(nvec)), dim3(256), 0, s, h, B, T, d, G, Tp, pad,
+                       (half_t*)zg, nvec);
+  else
+    hipLaunchKernelGGL(pos_pack_kernel<float>, dim3(grid_for(nvec)), dim3(256), 0, s, h, B, T, d, G, Tp, pad,
+                       (float*)zg, nvec);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_to_f32(DType t, const void* x, float* y, int64_t n, hipStream_t s) {
+  if (t == DType::F16)
+    hipLaunchKernelGGL(cast_to_f32_kernel<half_t>, dim3(grid_for(n)), dim3(256), 0, s, (const half_t*)x, y, n);
+  else
+    hipLaunchKernelGGL(cast_to_f32_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, (const float*)x, y, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_from_f32(DType t, const float* x, void* y, int64_t n, hipStream_t s) {
+  if (t == DType::F16)
+    hipLaunchKernelGGL(cast_from_f32_kernel<half_t>, dim3(grid_for(n)), dim3(256), 0, s, x, (half_t*)y, n);
+  else
+    hipLaunchKernelGGL(cast_from_f32_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, x, (float*)y, n);
+  return hipGetLastError();
+}
+
+}  // namespace w2v2

@@ -98,9 +98,10 @@ typedef enum { W2V2_FP32 = 0, W2V2_FP16 = 1 } w2v2_precision;
  *                  "Rewrites for the GPU").
  *
  * Supported limits (else W2V2_E_CONFIG): 1 <= n_conv <= 8, every conv_dim a
- * multiple of 8 and <= 2048, hidden and ffn multiples of 8, hidden <= 2048,
+ * multiple of 8 in [8, 2048] with conv_dim[0] <= 512, conv_kernel[0] <= 16,
+ * conv_stride[0] <= 64, hidden and ffn multiples of 8, hidden <= 2048,
  * (hidden / pos_groups) a multiple of 8, window long enough for >= 1 frame,
- * at most 32768 frames per window, 1 <= max_batch <= 4096.
+ * at most 16384 frames per window, 1 <= max_batch <= 4096.
  */
 typedef struct {
   int32_t abi_version; /* must be W2V2_ABI_VERSION */
@@ -236,7 +237,7 @@ w2v2_status w2v2_forward_encoder(w2v2_model* model, const float* features, int32
  *   lens    dev int32 [batch].
  * Needs no model; independent of w2v2_forward so that it can be fed any
  * logits (for example one-hot logits of a hand-written path).
- * Errors: W2V2_E_ARG (null pointer, batch < 1, frames < 1 or > 32768,
+ * Errors: W2V2_E_ARG (null pointer, batch < 1, frames < 1 or > 16384,
  * vocab < 1, blank_id outside [0, vocab)), W2V2_E_DEVICE.
  */
 w2v2_status w2v2_ctc_greedy(const float* logits, const int32_t* vframes, int32_t batch,
@@ -245,14 +246,16 @@ w2v2_status w2v2_ctc_greedy(const float* logits, const int32_t* vframes, int32_t
 
 /*
  * Per-kernel timing with HIP events.  When enabled, the model's calls record
- * an event pair around every kernel they launch (on the caller's stream).
+ * an event pair around every kernel they launch (on the caller's stream),
+ * or, if `only` is not NULL, around the launches whose kernel name equals
+ * `only` (so a timed loop can watch one kernel with two events per launch).
  * w2v2_profile_read synchronizes on the recorded events, accumulates the
  * per-kernel-name totals since the last read, and writes up to `cap`
  * entries: names[i] (static strings owned by the library), total_ms[i] and
  * launches[i].  *n receives the number of distinct kernel names.
  * Errors: W2V2_E_ARG, W2V2_E_DEVICE.
  */
-w2v2_status w2v2_profile_enable(w2v2_model* model, int32_t enable);
+w2v2_status w2v2_profile_enable(w2v2_model* model, int32_t enable, const char* only);
 w2v2_status w2v2_profile_read(w2v2_model* model, int32_t cap, const char** names, double* total_ms,
                               int64_t* launches, int32_t* n);
 

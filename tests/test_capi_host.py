@@ -161,7 +161,7 @@ def test_null_arguments_rejected():
     assert lib.w2v2_ctc_greedy(p, p, 1, 10, 32, 32, p, p, None) == L.E_ARG
     n = ctypes.c_int32()
     assert lib.w2v2_num_frames(None, 16000, ctypes.byref(n)) == L.E_ARG
-    assert lib.w2v2_profile_enable(None, 1) == L.E_ARG
+    assert lib.w2v2_profile_enable(None, 1, None) == L.E_ARG
     assert lib.w2v2_last_error().decode() != ""
 
 

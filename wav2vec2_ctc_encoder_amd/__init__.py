@@ -176,8 +176,10 @@ class Model:
         return logits
 
     # -- kernel timing ---------------------------------------------------
-    def profile_enable(self, on: bool = True) -> None:
-        _lib.check(_lib.lib().w2v2_profile_enable(self._h, int(bool(on))), "w2v2_profile_enable")
+    def profile_enable(self, on: bool = True, only: str | None = None) -> None:
+        """Time every kernel launch (or only launches of kernel ``only``) with HIP events."""
+        _lib.check(_lib.lib().w2v2_profile_enable(self._h, int(bool(on)), None if only is None else only.encode()),
+                   "w2v2_profile_enable")
 
     def profile_read(self) -> dict[str, tuple[float, int]]:
         """{kernel name: (total ms, launches)} since the previous read."""

@@ -89,7 +89,7 @@ def lib() -> ctypes.CDLL:
     L.w2v2_forward_encoder.restype = i32
     L.w2v2_ctc_greedy.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     L.w2v2_ctc_greedy.restype = i32
-    L.w2v2_profile_enable.argtypes = [vp, i32]
+    L.w2v2_profile_enable.argtypes = [vp, i32, ctypes.c_char_p]
     L.w2v2_profile_enable.restype = i32
     L.w2v2_profile_read.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(i64), ctypes.POINTER(i32)]

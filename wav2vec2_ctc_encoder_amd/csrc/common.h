@@ -14,6 +14,27 @@ enum class DType : int { F32 = 0, F16 = 1 };
 
 inline size_t dsize(DType t) { return t == DType::F16 ? 2 : 4; }
 
+// Exact (erf) GELU, x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), with erf from
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26
+// (Hastings' rational approximation, |error| <= 1.5e-7 for x >= 0):
+//   erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
+//   t = 1 / (1 + p z).
+// With e = poly(t) exp(-z^2) and z = |x| / sqrt 2, GELU(x) = x - x e / 2 for
+// x >= 0 and x e / 2 for x < 0.  Absolute error <= ~2e-7 |x| in fp32, far
+// below the fp16 operand rounding the fp16 mode adds; GELU(0) is exactly 0.
+__device__ inline float gelu_erf(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float p = fmaf(1.061405429f, t, -1.453152027f);
+  p = fmaf(p, t, 1.421413741f);
+  p = fmaf(p, t, -0.284496736f);
+  p = fmaf(p, t, 0.254829592f);
+  p *= t;
+  const float e = p * __builtin_amdgcn_exp2f(-(z * z) * 1.4426950408889634f);
+  const float h = 0.5f * x * e;
+  return x >= 0.f ? x - h : h;
+}
+
 // Kernel-timing hook of the runtime: called around every launch.
 struct LaunchHook {
   virtual void before(const char* name, hipStream_t s) = 0;
@@ -32,7 +53,15 @@ struct LaunchHook {
 //   stores fp32 (out_f32) and/or operand type (out_t) at C + group*c_group + m*ldc + n.
 //   grid.z = groups.
 // ----------------------------------------------------------------------------
+// Role of a GEMM launch.  Each role is compiled as its own kernel symbol so
+// profilers attribute time per role.
+enum GemmRole : int {
+  kGemmConv = 0, kGemmProj = 1, kGemmPos = 2, kGemmQKV = 3, kGemmOut = 4, kGemmFFN1 = 5, kGemmFFN2 = 6,
+  kGemmHead = 7, kGemmRoles = 8
+};
+
 struct GemmArgs {
+  int32_t role = kGemmConv;
   const void* A = nullptr;
   int64_t lda = 0, a_seg = 0, a_group = 0;
   int32_t seg_rows = 1;

@@ -26,8 +26,6 @@ namespace {
 constexpr int kChunk = 256;  // frames per workgroup
 constexpr int kLanesC = 8;   // channels per lane
 
-__device__ inline float gelu_exact(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
-
 __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -125,7 +123,7 @@ __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pc
       }
       const float rstd = rsqrtf(wave_sum(q) * invC + eps);
 #pragma unroll
-      for (int c = 0; c < kLanesC; ++c) v[c] = gelu_exact((v[c] - mean) * rstd * g[c] + be[c]);
+      for (int c = 0; c < kLanesC; ++c) v[c] = gelu_erf((v[c] - mean) * rstd * g[c] + be[c]);
       if (active) store8<T>(y + ((int64_t)b * T0 + t0 + f) * C + c0, v);
     }
     return;
@@ -221,7 +219,7 @@ __global__ __launch_bounds__(256) void gn_apply_gelu_kernel(T* __restrict__ y, c
 #pragma unroll
     for (int i = 0; i < EPV; ++i) {
       const float2 p = s[i];
-      el[i] = (T)gelu_exact(fmaf((float)el[i], p.x, p.y));
+      el[i] = (T)gelu_erf(fmaf((float)el[i], p.x, p.y));
     }
     *(uint4*)(y + e) = raw;
   }

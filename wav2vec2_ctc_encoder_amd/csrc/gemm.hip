@@ -55,7 +55,7 @@ struct Mma<float> {
   }
 };
 
-__device__ inline float gelu_exact(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+
 
 // Spread consecutive workgroups of one XCD over a contiguous range of tiles:
 // the dispatcher hands workgroup ids to the 8 XCDs round-robin, and each XCD
@@ -67,7 +67,51 @@ __device__ inline int xcd_remap(int pid, int nb) {
   return x * per + (x < rem ? x : rem) + local;
 }
 
-template <typename T, int BM, int BN, int WM, int WN>
+// Epilogue for 4 consecutive output columns nb..nb+3 of row m:
+// v = acc + bias; v = act(v); v += residual; store fp32 and/or operand type.
+template <typename T>
+__device__ inline void epilogue4(const GemmArgs& a, const float* bias, int64_t rowoff, int nb, f4 v, bool vec) {
+  if (vec) {
+    if (bias) {
+      const float4 bb = *(const float4*)(bias + nb);
+      v.x += bb.x; v.y += bb.y; v.z += bb.z; v.w += bb.w;
+    }
+    if (a.act == 1) {
+      v.x = gelu_erf(v.x); v.y = gelu_erf(v.y); v.z = gelu_erf(v.z); v.w = gelu_erf(v.w);
+    }
+    if (a.residual) {
+      const float4 rr = *(const float4*)(a.residual + rowoff + nb);
+      v.x += rr.x; v.y += rr.y; v.z += rr.z; v.w += rr.w;
+    }
+    if (a.out_f32) *(float4*)(a.out_f32 + rowoff + nb) = make_float4(v.x, v.y, v.z, v.w);
+    if (a.out_t) {
+      if constexpr (sizeof(T) == 2) {
+        h4 hv = {(half_t)v.x, (half_t)v.y, (half_t)v.z, (half_t)v.w};
+        *(h4*)((half_t*)a.out_t + rowoff + nb) = hv;
+      } else {
+        *(float4*)((float*)a.out_t + rowoff + nb) = make_float4(v.x, v.y, v.z, v.w);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = nb + r;
+      if (n >= a.N) break;
+      float x = v[r];
+      if (bias) x += bias[n];
+      if (a.act == 1) x = gelu_erf(x);
+      if (a.residual) x += a.residual[rowoff + n];
+      if (a.out_f32) a.out_f32[rowoff + n] = x;
+      if (a.out_t) ((T*)a.out_t)[rowoff + n] = (T)x;
+    }
+  }
+}
+
+__device__ inline bool epilogue_vec_ok(const GemmArgs& a) {
+  return ((a.ldc & 3) == 0) && ((a.N & 3) == 0) && ((a.c_group & 3) == 0) && ((a.bias_group & 3) == 0);
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int ROLE>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   constexpr int TM = BM / WM / 16;
   constexpr int TN = BN / WN / 16;
@@ -186,8 +230,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   }
 
   // epilogue: lane holds rows m, columns nb .. nb+3
-  const bool vec = ((a.ldc & 3) == 0) && ((a.N & 3) == 0) && ((a.c_group & 3) == 0) &&
-                   ((a.bias_group & 3) == 0);
+  const bool vec = epilogue_vec_ok(a);
   const float* bias = a.bias ? a.bias + (int64_t)group * a.bias_group : nullptr;
   const int64_t cg = (int64_t)group * a.c_group;
 #pragma unroll
@@ -198,66 +241,394 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
       const int nb = n0 + wn * TN * 16 + i * 16 + lg * 4;
-      if (nb >= a.N) continue;
-      f4 v = acc[i][j];
-      if (vec) {
-        if (bias) {
-          const float4 bb = *(const float4*)(bias + nb);
-          v.x += bb.x; v.y += bb.y; v.z += bb.z; v.w += bb.w;
-        }
-        if (a.act == 1) {
-          v.x = gelu_exact(v.x); v.y = gelu_exact(v.y); v.z = gelu_exact(v.z); v.w = gelu_exact(v.w);
-        }
-        if (a.residual) {
-          const float4 rr = *(const float4*)(a.residual + rowoff + nb);
-          v.x += rr.x; v.y += rr.y; v.z += rr.z; v.w += rr.w;
-        }
-        if (a.out_f32) *(float4*)(a.out_f32 + rowoff + nb) = make_float4(v.x, v.y, v.z, v.w);
-        if (a.out_t) {
-          if constexpr (sizeof(T) == 2) {
-            h4 hv = {(half_t)v.x, (half_t)v.y, (half_t)v.z, (half_t)v.w};
-            *(h4*)((half_t*)a.out_t + rowoff + nb) = hv;
-          } else {
-            *(float4*)((float*)a.out_t + rowoff + nb) = make_float4(v.x, v.y, v.z, v.w);
-          }
-        }
-      } else {
+      if (nb < a.N) epilogue4<T>(a, bias, rowoff, nb, acc[i][j], vec);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// fp16 kernel on v_mfma_f32_32x32x16_f16 with large wave tiles.
+// A wave owns (TN*32) x (TM*32) outputs; per 16-wide K slice it reads TN + TM
+// fragments from LDS and issues TN*TM MFMAs, so a 128x128 wave tile needs
+// half the LDS bytes per flop of the 64x64 / 16x16 layout above.  In the
+// 32x32 output block a lane holds activation row (lane % 32) and weight
+// columns 8q + 4*(lane / 32) + {0..3}, q = 0..3.
+// ----------------------------------------------------------------------------
+typedef float f16x __attribute__((ext_vector_type(16)));
+
+template <int BM, int BN, int WM, int WN, int ROLE>
+__global__ __launch_bounds__(256, 1) void gemm_f16_kernel(GemmArgs a) {
+  constexpr int TM = BM / WM / 32;
+  constexpr int TN = BN / WN / 32;
+  constexpr int BK = 64;                 // halves per 128-byte tile row
+  constexpr int NLA = BM * 8 / 256;
+  constexpr int NLB = BN * 8 / 256;
+  static_assert(WM * WN == 4 && TM >= 1 && TN >= 1, "4 waves");
+
+  __shared__ uint4 sA[2][BM * kPitch];
+  __shared__ uint4 sB[2][BN * kPitch];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int group = blockIdx.z;
+
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles_n = (a.N + BN - 1) / BN;
+  const int pid = xcd_remap(blockIdx.x, gridDim.x);
+  constexpr int GM = 8;
+  const int width = GM * tiles_n;
+  const int first_m = (pid / width) * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int tm = first_m + (pid % width) % gsz;
+  const int tn = (pid % width) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const char* Abase = (const char*)a.A + (int64_t)group * a.a_group * 2;
+  const char* Bbase = (const char*)a.B + (int64_t)group * a.b_group * 2;
+
+  const char* arow[NLA];
+  bool aok[NLA];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int n = nb + r;
-          if (n >= a.N) break;
-          float x = v[r];
-          if (bias) x += bias[n];
-          if (a.act == 1) x = gelu_exact(x);
-          if (a.residual) x += a.residual[rowoff + n];
-          if (a.out_f32) a.out_f32[rowoff + n] = x;
-          if (a.out_t) ((T*)a.out_t)[rowoff + n] = (T)x;
+  for (int i = 0; i < NLA; ++i) {
+    const int idx = tid + 256 * i;
+    const int m = m0 + (idx >> 3);
+    aok[i] = m < a.M;
+    const int mm = aok[i] ? m : 0;
+    const int seg = mm / a.seg_rows, t = mm - seg * a.seg_rows;
+    arow[i] = Abase + ((int64_t)seg * a.a_seg + (int64_t)t * a.lda) * 2 + (idx & 7) * 16;
+  }
+  const char* brow[NLB];
+  bool bok[NLB];
+#pragma unroll
+  for (int i = 0; i < NLB; ++i) {
+    const int idx = tid + 256 * i;
+    const int n = n0 + (idx >> 3);
+    bok[i] = n < a.N;
+    brow[i] = Bbase + ((int64_t)(bok[i] ? n : 0) * a.K) * 2 + (idx & 7) * 16;
+  }
+
+  uint4 ra[NLA], rb[NLB];
+  auto load = [&](int kt) {
+    const int kbase = kt * BK;
+#pragma unroll
+    for (int i = 0; i < NLA; ++i) {
+      const int idx = tid + 256 * i;
+      const bool ok = aok[i] && (kbase + (idx & 7) * 8 < a.K);
+      ra[i] = ok ? *(const uint4*)(arow[i] + (int64_t)kbase * 2) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NLB; ++i) {
+      const int idx = tid + 256 * i;
+      const bool ok = bok[i] && (kbase + (idx & 7) * 8 < a.K);
+      rb[i] = ok ? *(const uint4*)(brow[i] + (int64_t)kbase * 2) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NLA; ++i) {
+      const int idx = tid + 256 * i;
+      sA[buf][(idx >> 3) * kPitch + (idx & 7)] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NLB; ++i) {
+      const int idx = tid + 256 * i;
+      sB[buf][(idx >> 3) * kPitch + (idx & 7)] = rb[i];
+    }
+  };
+
+  f16x acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk = (a.K + BK - 1) / BK;
+  load(0);
+  store(0);
+  __syncthreads();
+
+  const int l32 = lane & 31, lg = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 wv[TN], av[TM];
+#pragma unroll
+      for (int i = 0; i < TN; ++i) wv[i] = sB[cur][(wn * TN * 32 + i * 32 + l32) * kPitch + ks * 2 + lg];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) av[j] = sA[cur][(wm * TM * 32 + j * 32 + l32) * kPitch + ks * 2 + lg];
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, wv[i]),
+                                                             __builtin_bit_cast(h8, av[j]), acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store(cur ^ 1);
+    __syncthreads();
+  }
+
+  const bool vec = epilogue_vec_ok(a);
+  const float* bias = a.bias ? a.bias + (int64_t)group * a.bias_group : nullptr;
+  const int64_t cg = (int64_t)group * a.c_group;
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int m = m0 + wm * TM * 32 + j * 32 + l32;
+    if (m >= a.M) continue;
+    const int64_t rowoff = cg + (int64_t)m * a.ldc;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nb = n0 + wn * TN * 32 + i * 32 + 8 * q + 4 * lg;
+        if (nb < a.N) {
+          const f4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          epilogue4<half_t>(a, bias, rowoff, nb, v, vec);
         }
       }
     }
   }
 }
 
-template <typename T, int BM, int BN, int WM, int WN>
+// ----------------------------------------------------------------------------
+// fp16 kernel with direct global->LDS loads (gfx950 global_load_lds_dwordx4)
+// and a STAGES-deep LDS ring.  Requires K % 64 == 0.
+//
+// Each wave-wide load instruction moves 1 KB: lane l's 16 bytes land at LDS
+// base + 16*l, i.e. 8 tile rows of 128 bytes.  Lane l therefore fetches row
+// r = 8*j + l/8 of its slice and the global chunk c = (l % 8) ^ ((r / 2) % 8),
+// so the row's chunks sit XOR-swizzled in LDS and the MFMA fragment reads
+// (16 lanes on 16 consecutive rows, same chunk) hit 16 distinct bank groups.
+// Rows beyond M or N are clamped to the last valid row (their outputs are
+// never stored), so every load is unconditional and in bounds.
+//
+// Pipeline: loads for K step kt + STAGES - 1 are issued right after the
+// barrier that publishes step kt, and step kt waits (vmcnt) only for its own
+// loads, so STAGES - 1 steps stay in flight during the MFMA work.
+// ----------------------------------------------------------------------------
+// One wave-wide direct global->LDS load: lane l's 16 bytes at gptr land at
+// LDS byte address lds + 16*l.  Written as inline asm so that the compiler's
+// wait-count pass does not treat every later LDS read as dependent on it (it
+// would wait for all outstanding loads, serialising the pipeline); the
+// kernel waits on vmcnt explicitly.  The instruction has no result register.
+__device__ inline void dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, int BKB, int ROLE>
+__global__ __launch_bounds__(256, 1) void gemm_dlds_kernel(GemmArgs a) {
+  constexpr int TM = BM / WM / 32;
+  constexpr int TN = BN / WN / 32;
+  constexpr int CPR = BKB / 16;          // 16-byte chunks per tile row (8 or 4)
+  constexpr int RPI = 64 / CPR;          // tile rows per 1 KB wave load
+  constexpr int KEYDIV = 16 / CPR;       // rows sharing a bank-group phase
+  constexpr int KS = BKB / 32;           // 16-wide K slices per step
+  constexpr int JA = BM / RPI / 4;       // 1 KB load instructions per wave per stage (A)
+  constexpr int JB = BN / RPI / 4;       // (B)
+  constexpr int LPS = JA + JB;           // loads per thread per stage
+  static_assert(WM * WN == 4 && TM >= 1 && TN >= 1, "4 waves");
+  static_assert(JA >= 1 && JB >= 1 && LPS <= 15, "tile / vmcnt range");
+
+  __shared__ uint4 sA[STAGES][BM * CPR];
+  __shared__ uint4 sB[STAGES][BN * CPR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int group = blockIdx.z;
+
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles_n = (a.N + BN - 1) / BN;
+  const int pid = xcd_remap(blockIdx.x, gridDim.x);
+  constexpr int GM = 8;
+  const int width = GM * tiles_n;
+  const int first_m = (pid / width) * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int tm = first_m + (pid % width) % gsz;
+  const int tn = (pid % width) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const char* Abase = (const char*)a.A + (int64_t)group * a.a_group * 2;
+  const char* Bbase = (const char*)a.B + (int64_t)group * a.b_group * 2;
+
+  // source rows (clamped) with the swizzled chunk folded in
+  const int pos = lane & (CPR - 1);
+  const char* asrc[JA];
+#pragma unroll
+  for (int j = 0; j < JA; ++j) {
+    const int r = (wave * JA + j) * RPI + lane / CPR;
+    const int m = min(m0 + r, a.M - 1);
+    const int seg = m / a.seg_rows, t = m - seg * a.seg_rows;
+    asrc[j] = Abase + ((int64_t)seg * a.a_seg + (int64_t)t * a.lda) * 2 +
+              ((pos ^ ((r / KEYDIV) & (CPR - 1))) << 4);
+  }
+  const char* bsrc[JB];
+#pragma unroll
+  for (int j = 0; j < JB; ++j) {
+    const int r = (wave * JB + j) * RPI + lane / CPR;
+    const int n = min(n0 + r, a.N - 1);
+    bsrc[j] = Bbase + (int64_t)n * a.K * 2 + ((pos ^ ((r / KEYDIV) & (CPR - 1))) << 4);
+  }
+
+  const uint32_t ldsA = (uint32_t)(uintptr_t)&sA[0][0], ldsB = (uint32_t)(uintptr_t)&sB[0][0];
+  auto issue = [&](int kt, int buf) {
+    const int64_t koff = (int64_t)kt * BKB;
+#pragma unroll
+    for (int j = 0; j < JA; ++j)
+      dma16(asrc[j] + koff,
+            __builtin_amdgcn_readfirstlane(ldsA + (uint32_t)((buf * BM * CPR + (wave * JA + j) * 64) * 16)));
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+      dma16(bsrc[j] + koff,
+            __builtin_amdgcn_readfirstlane(ldsB + (uint32_t)((buf * BN * CPR + (wave * JB + j) * 64) * 16)));
+  };
+
+  f16x acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk = a.K / (BKB / 2);
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue(st, st);
+
+  const int l32 = lane & 31, lg = lane >> 5;
+  // per-lane LDS row offsets (uint4 units) and swizzle keys of the fragment rows
+  int arow[TM], akey[TM], brow[TN], bkey[TN];
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int R = wm * TM * 32 + j * 32 + l32;
+    arow[j] = R * CPR;
+    akey[j] = (R / KEYDIV) & (CPR - 1);
+  }
+#pragma unroll
+  for (int i = 0; i < TN; ++i) {
+    const int R = wn * TN * 32 + i * 32 + l32;
+    brow[i] = R * CPR;
+    bkey[i] = (R / KEYDIV) & (CPR - 1);
+  }
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // wait for this step's loads (later steps may stay in flight), publish
+    if (kt + 1 < nk && STAGES > 2)
+      __builtin_amdgcn_s_waitcnt((LPS & 0xF) | ((LPS >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    else
+      __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
+    __builtin_amdgcn_s_barrier();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    const int buf = kt % STAGES;
+    const uint4* A_ = sA[buf];
+    const uint4* B_ = sB[buf];
+    uint4 wv[2][TN], av[2][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) wv[0][i] = B_[brow[i] + ((0 * 2 + lg) ^ bkey[i])];
+#pragma unroll
+    for (int j = 0; j < TM; ++j) av[0][j] = A_[arow[j] + ((0 * 2 + lg) ^ akey[j])];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int i = 0; i < TN; ++i) wv[cur ^ 1][i] = B_[brow[i] + (((ks + 1) * 2 + lg) ^ bkey[i])];
+#pragma unroll
+        for (int j = 0; j < TM; ++j) av[cur ^ 1][j] = A_[arow[j] + (((ks + 1) * 2 + lg) ^ akey[j])];
+      }
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, wv[cur][i]),
+                                                             __builtin_bit_cast(h8, av[cur][j]), acc[i][j], 0, 0, 0);
+    }
+    // all LDS reads of this buffer have been consumed by the MFMAs above;
+    // make sure they completed before the next barrier lets the buffer refill
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+  }
+
+  const bool vec = epilogue_vec_ok(a);
+  const float* bias = a.bias ? a.bias + (int64_t)group * a.bias_group : nullptr;
+  const int64_t cg = (int64_t)group * a.c_group;
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int m = m0 + wm * TM * 32 + j * 32 + l32;
+    if (m >= a.M) continue;
+    const int64_t rowoff = cg + (int64_t)m * a.ldc;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nb = n0 + wn * TN * 32 + i * 32 + 8 * q + 4 * lg;
+        if (nb < a.N) {
+          const f4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          epilogue4<half_t>(a, bias, rowoff, nb, v, vec);
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int ROLE>
 hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN>), dim3(tiles, 1, a.groups), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, ROLE>), dim3(tiles, 1, a.groups), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
+template <int BM, int BN, int ST, int BKB, int ROLE>
+hipError_t launch_dlds(const GemmArgs& a, hipStream_t s) {
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_dlds_kernel<BM, BN, 2, 2, ST, BKB, ROLE>), dim3(tiles, 1, a.groups), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int ROLE>
+hipError_t launch_shape(const GemmArgs& a, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    // direct-to-LDS pipeline: whole 64-wide K steps, N wide enough to fill a tile
+    if (a.K % 64 == 0 && a.N > 32) {
+      const int64_t tiles128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.groups;
+      // 128x128 tiles are the most efficient per flop; with fewer than four
+      // rounds of two tiles per CU, 128x64 tiles balance the CUs better.
+      if (a.N > 64 && tiles128 >= 1024) return launch_dlds<128, 128, 2, 128, ROLE>(a, s);
+      return launch_dlds<128, 64, 2, 128, ROLE>(a, s);
+    }
+  }
+  if (a.N <= 32) return launch_t<T, 128, 32, 4, 1, ROLE>(a, s);
+  if (a.N <= 48) return launch_t<T, 128, 48, 4, 1, ROLE>(a, s);
+  if (a.N <= 64) return launch_t<T, 128, 64, 4, 1, ROLE>(a, s);
+  return launch_t<T, 128, 128, 2, 2, ROLE>(a, s);
+}
+
 template <typename T>
-hipError_t launch_dispatch(const GemmArgs& a, hipStream_t s) {
-  if (a.N <= 32) return launch_t<T, 128, 32, 4, 1>(a, s);
-  if (a.N <= 48) return launch_t<T, 128, 48, 4, 1>(a, s);
-  if (a.N <= 64) return launch_t<T, 128, 64, 4, 1>(a, s);
-  return launch_t<T, 128, 128, 2, 2>(a, s);
+hipError_t launch_role(const GemmArgs& a, hipStream_t s) {
+  switch (a.role) {
+    case kGemmConv: return launch_shape<T, kGemmConv>(a, s);
+    case kGemmProj: return launch_shape<T, kGemmProj>(a, s);
+    case kGemmPos: return launch_shape<T, kGemmPos>(a, s);
+    case kGemmQKV: return launch_shape<T, kGemmQKV>(a, s);
+    case kGemmOut: return launch_shape<T, kGemmOut>(a, s);
+    case kGemmFFN1: return launch_shape<T, kGemmFFN1>(a, s);
+    case kGemmFFN2: return launch_shape<T, kGemmFFN2>(a, s);
+    case kGemmHead: return launch_shape<T, kGemmHead>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_gemm(DType t, const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0 || a.K <= 0 || a.groups <= 0) return hipSuccess;
-  return t == DType::F16 ? launch_dispatch<half_t>(a, s) : launch_dispatch<float>(a, s);
+  return t == DType::F16 ? launch_role<half_t>(a, s) : launch_role<float>(a, s);
 }
 
 }  // namespace w2v2

@@ -240,6 +240,7 @@ struct w2v2_model {
 
   Profiler* prof = nullptr;
   bool prof_on = false;
+  std::string prof_only;  // empty: every kernel
 
   ~w2v2_model() {
     delete prof;
@@ -271,9 +272,10 @@ size_t add_t(Arena& a, DType dt, const std::vector<float>& v) {
 
 #define W2V2_LAUNCH(m, s, name, call)                                                 \
   do {                                                                                \
-    if ((m)->prof_on) (m)->prof->before(name, s);                                     \
+    const bool p_ = (m)->prof_on && ((m)->prof_only.empty() || (m)->prof_only == name); \
+    if (p_) (m)->prof->before(name, s);                                               \
     hipError_t e_ = (call);                                                           \
-    if ((m)->prof_on) (m)->prof->after(name, s);                                      \
+    if (p_) (m)->prof->after(name, s);                                                \
     if (e_ != hipSuccess)                                                             \
       return fail(W2V2_E_DEVICE, std::string(name) + ": " + hipGetErrorString(e_));  \
   } while (0)
@@ -304,6 +306,7 @@ w2v2_status run_frontend(w2v2_model* m, const float* pcm, const int32_t* valid, 
   for (int i = 1; i < c.n_conv; ++i) {
     void* out = (i & 1) ? m->bufB : m->bufA;
     GemmArgs g;
+    g.role = kGemmConv;
     g.A = cur;
     g.lda = (int64_t)c.conv_stride[i] * cin;
     g.a_seg = (int64_t)tin * cin;
@@ -330,10 +333,11 @@ w2v2_status run_frontend(w2v2_model* m, const float* pcm, const int32_t* valid, 
   return W2V2_OK;
 }
 
-w2v2_status gemm_linear(w2v2_model* m, hipStream_t s, const char* name, const void* A, int M, int N, int K,
-                        const void* W, const float* bias, int act, const float* residual, float* out32,
+w2v2_status gemm_linear(w2v2_model* m, hipStream_t s, const char* name, int role, const void* A, int M, int N,
+                        int K, const void* W, const float* bias, int act, const float* residual, float* out32,
                         void* outt, int64_t ldc) {
   GemmArgs g;
+  g.role = role;
   g.A = A;
   g.lda = K;
   g.a_seg = 0;
@@ -369,13 +373,14 @@ w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, h
   // feature projection: LN over channels, then Linear C -> d (fp32 residual stream)
   W2V2_LAUNCH(m, s, "layernorm",
               launch_layernorm(dt, nullptr, feat, M, cl, m->fp_g, m->fp_b, eps, nullptr, m->x, 0, s));
-  W2V2_TRY(gemm_linear(m, s, "gemm_feature_proj", m->x, M, d, cl, m->fp_w, m->fp_bias, 0, nullptr, m->h, nullptr, d));
+  W2V2_TRY(gemm_linear(m, s, "gemm_feature_proj", kGemmProj, m->x, M, d, cl, m->fp_w, m->fp_bias, 0, nullptr, m->h, nullptr, d));
 
   // positional conv: h = z + GELU(posconv(z) + bias)
   const int pad = K / 2;
   W2V2_LAUNCH(m, s, "pos_pack", launch_pos_pack(dt, m->h, B, T, d, G, K, pad, m->zg, s));
   {
     GemmArgs g;
+    g.role = kGemmPos;
     g.A = m->zg;
     g.lda = Cg;
     g.a_seg = (int64_t)(T + K) * Cg;
@@ -406,17 +411,17 @@ w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, h
     if (stable)
       W2V2_LAUNCH(m, s, "layernorm",
                   launch_layernorm(dt, m->h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, nullptr, m->x, 0, s));
-    W2V2_TRY(gemm_linear(m, s, "gemm_qkv", m->x, M, 3 * d, d, L.wqkv, L.bqkv, 0, nullptr, nullptr, m->qkv, 3 * d));
+    W2V2_TRY(gemm_linear(m, s, "gemm_qkv", kGemmQKV, m->x, M, 3 * d, d, L.wqkv, L.bqkv, 0, nullptr, nullptr, m->qkv, 3 * d));
     W2V2_LAUNCH(m, s, "attention", launch_attention(dt, m->qkv, m->attn, B, T, c.heads, d / c.heads, s));
-    W2V2_TRY(gemm_linear(m, s, "gemm_out_proj", m->attn, M, d, d, L.wo, L.bo, 0, m->h, m->h, nullptr, d));
+    W2V2_TRY(gemm_linear(m, s, "gemm_out_proj", kGemmOut, m->attn, M, d, d, L.wo, L.bo, 0, m->h, m->h, nullptr, d));
     if (stable)
       W2V2_LAUNCH(m, s, "layernorm",
                   launch_layernorm(dt, m->h, nullptr, M, d, L.ln2_g, L.ln2_b, eps, nullptr, m->x, 0, s));
     else
       W2V2_LAUNCH(m, s, "layernorm",
                   launch_layernorm(dt, m->h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, m->h, m->x, 0, s));
-    W2V2_TRY(gemm_linear(m, s, "gemm_ffn1", m->x, M, F, d, L.w1, L.b1, 1, nullptr, nullptr, m->ffn, F));
-    W2V2_TRY(gemm_linear(m, s, "gemm_ffn2", m->ffn, M, d, F, L.w2, L.b2, 0, m->h, m->h, nullptr, d));
+    W2V2_TRY(gemm_linear(m, s, "gemm_ffn1", kGemmFFN1, m->x, M, F, d, L.w1, L.b1, 1, nullptr, nullptr, m->ffn, F));
+    W2V2_TRY(gemm_linear(m, s, "gemm_ffn2", kGemmFFN2, m->ffn, M, d, F, L.w2, L.b2, 0, m->h, m->h, nullptr, d));
     if (!stable)
       W2V2_LAUNCH(m, s, "layernorm",
                   launch_layernorm(dt, m->h, nullptr, M, d, L.ln2_g, L.ln2_b, eps, m->h, m->x, 0, s));
@@ -424,7 +429,7 @@ w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, h
   if (stable)
     W2V2_LAUNCH(m, s, "layernorm",
                 launch_layernorm(dt, m->h, nullptr, M, d, m->enc_g, m->enc_b, eps, nullptr, m->x, 0, s));
-  W2V2_TRY(gemm_linear(m, s, "gemm_ctc_head", m->x, M, c.vocab, d, m->head_w, m->head_b, 0, nullptr, logits,
+  W2V2_TRY(gemm_linear(m, s, "gemm_ctc_head", kGemmHead, m->x, M, c.vocab, d, m->head_w, m->head_b, 0, nullptr, logits,
                        nullptr, c.vocab));
   return W2V2_OK;
 }
@@ -794,10 +799,11 @@ w2v2_status w2v2_ctc_greedy(const float* logits, const int32_t* vframes, int32_t
   return W2V2_OK;
 }
 
-w2v2_status w2v2_profile_enable(w2v2_model* m, int32_t enable) {
+w2v2_status w2v2_profile_enable(w2v2_model* m, int32_t enable, const char* only) {
   if (!m) return fail(W2V2_E_ARG, "model is NULL");
   if (enable && !m->prof) m->prof = new Profiler();
   m->prof_on = enable != 0;
+  m->prof_only = only ? only : "";
   return W2V2_OK;
 }
 

@@ -14,8 +14,6 @@ namespace {
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
-__device__ inline float gelu_exact(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
-
 __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -89,7 +87,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const XT* x, int64_t R, 
       o.z = (v[i].z - mean) * rstd * g.z + b.z;
       o.w = (v[i].w - mean) * rstd * g.w + b.w;
       if (act == 1) {
-        o.x = gelu_exact(o.x); o.y = gelu_exact(o.y); o.z = gelu_exact(o.z); o.w = gelu_exact(o.w);
+        o.x = gelu_erf(o.x); o.y = gelu_erf(o.y); o.z = gelu_erf(o.z); o.w = gelu_erf(o.w);
       }
       if (y32) *(float4*)(y32 + row * C + c) = o;
       if (yt) store4<T>(yt + row * C + c, o);

@@ -35,7 +35,7 @@ PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
-FRONTEND_KERNELS = {"conv0_gn_stats", "gn_finalize", "gn_apply_gelu", "conv0_ln_gelu", "conv_gemm", "conv_ln_gelu"}
+FRONTEND_KERNELS = {"gn0_stats", "gn0_finalize", "conv0_gn_gelu", "conv0_ln_gelu", "conv_gemm", "conv_ln_gelu"}
 
 
 def frames(n, ks, ss):
@@ -62,9 +62,9 @@ def algorithmic_work(cfg, B: int, dsize: int) -> dict[str, tuple[str, float]]:
     conv_flop = sum(2.0 * B * T[i] * C[i] * cfg.conv_kernel[i] * C[i - 1] for i in range(1, len(C)))
     w["conv_gemm"] = ("flop", conv_flop)
     if cfg.feat_norm == "group":
-        nchunk = -(-T[0] // 256)
-        w["conv0_gn_stats"] = ("byte", B * cfg.window * 4.0 + B * T[0] * C[0] * dsize + B * nchunk * C[0] * 8.0)
-        w["gn_apply_gelu"] = ("byte", 2.0 * B * T[0] * C[0] * dsize)
+        # conv0 + GroupNorm + GELU: read the PCM, write the normalised output once
+        w["conv0_gn_gelu"] = ("byte", B * cfg.window * 4.0 + B * T[0] * C[0] * dsize)
+        w["gn0_stats"] = ("byte", B * cfg.window * 4.0)
     else:
         w["conv0_ln_gelu"] = ("byte", B * cfg.window * 4.0 + B * T[0] * C[0] * dsize)
         w["conv_ln_gelu"] = ("byte", sum(2.0 * B * T[i] * C[i] * dsize for i in range(1, len(C))))

@@ -83,24 +83,28 @@ hipError_t launch_gemm(DType t, const GemmArgs& a, hipStream_t s);
 // ----------------------------------------------------------------------------
 // feature-encoder kernels
 // ----------------------------------------------------------------------------
-// conv 0 (one input channel) over the zero-padded window.
-//   pcm [B, L] fp32, valid [B]; w0 [C][k] fp32; bias [C] fp32 or null.
-//   group variant (stats != null): y [B, T0, C] (type t) = conv, plus per
-//     (b, chunk, c) partial (mean, M2) over the chunk's frames.
+// conv 0 (one input channel) over the zero-padded window, fused with its
+// norm and GELU:
+//   pcm [B, L] fp32, valid [B]; w0 [C][k] fp32; bias [C] fp32 or null;
+//   y [B, T0, C] (operand type).
+//   group variant (gamma == null): y = GELU(conv * ss[b, c].x + ss[b, c].y),
+//     ss from gn0_finalize.
 //   layer variant (gamma != null): y = GELU(LN_c(conv + bias) * gamma + beta).
-int conv0_chunk_frames();
 hipError_t launch_conv0(DType t, const float* pcm, const int32_t* valid, int32_t L, int32_t B,
                         const float* w0, const float* bias, int32_t C, int32_t k, int32_t stride,
-                        int32_t T0, void* y, float2* stats, const float* gamma, const float* beta,
+                        int32_t T0, void* y, const float2* ss, const float* gamma, const float* beta,
                         float eps, hipStream_t s);
-// GroupNorm finalize: chunk partials -> per (b, c) scale = gamma*rstd and
-// shift = beta - mean*gamma*rstd.
-hipError_t launch_gn_finalize(const float2* stats, int32_t B, int32_t C, int32_t T0, int32_t chunk,
-                              const float* gamma, const float* beta, float eps, float2* scale_shift,
-                              hipStream_t s);
-// y = GELU(y * scale[b, c] + shift[b, c]) in place on [B, T, C].
-hipError_t launch_gn_apply_gelu(DType t, void* y, const float2* scale_shift, int32_t B, int32_t T,
-                                int32_t C, hipStream_t s);
+// GroupNorm statistics of conv 0 from the PCM alone: per-chunk means and
+// co-moments of the k shifted sample sequences (fp64), then per (b, c)
+// scale = gamma * rstd and shift = beta - mean * scale.
+// Workspace: B * gn0_partial_doubles(k, T0) doubles (chunk partials, then the
+// per-row merged statistics behind them).
+int64_t gn0_partial_doubles(int32_t k, int32_t T0);  // per row
+hipError_t launch_gn0_stats(const float* pcm, const int32_t* valid, int32_t L, int32_t B, int32_t k, int32_t stride,
+                            int32_t T0, double* part, hipStream_t s);
+hipError_t launch_gn0_finalize(double* part, int32_t B, int32_t k, int32_t T0, const float* w0, const float* bias,
+                               int32_t C, const float* gamma, const float* beta, float eps, float2* ss,
+                               hipStream_t s);
 
 // ----------------------------------------------------------------------------
 // row kernels

@@ -10,12 +10,16 @@
 // single 1 KB (fp16) coalesced store per wave.
 //
 // Group-norm variant: GroupNorm with one group per channel needs mean and
-// variance over all T0 frames of a row.  Each workgroup writes, per channel,
-// the mean and the centred sum of squares M2 of its own chunk (computed in
-// two passes over the chunk, the second recomputing the 10-tap conv from
-// LDS instead of re-reading the output); gn_finalize merges the chunk
-// partials in a fixed order with Chan's pairwise update, so the statistics
-// are deterministic and free of the cancellation of sum / sum-of-squares.
+// variance over all T0 frames of a row.  Conv 0 is linear in the k shifted
+// sample sequences x_j(t) = x[s*t + j], so with mu_j their means and
+// S_ij = sum_t (x_i(t) - mu_i)(x_j(t) - mu_j) their co-moments, channel c
+// (taps w_c, bias b_c) has mean w_c . mu + b_c and variance w_c^T S w_c / T0.
+// gn0_stats reads only the PCM and writes per-chunk (mu, S) partials in
+// fp64; gn0_finalize merges them in a fixed order with Chan's pairwise
+// update and forms each channel's scale and shift; conv0 then applies
+// GroupNorm and GELU before its single store, so the pre-norm conv output
+// never goes to memory.  Deterministic, and fp64 keeps the quadratic form
+// accurate even when a filter cancels most of the input's energy.
 // Layer-norm variant: the per-frame LayerNorm over channels and the GELU are
 // done in registers with wave reductions before the single store.
 #include "common.h"
@@ -54,7 +58,7 @@ template <typename T, int KT>
 __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pcm, const int32_t* __restrict__ valid,
                                                      int L, const float* __restrict__ w0,
                                                      const float* __restrict__ bias, int C, int k, int stride,
-                                                     int T0, T* __restrict__ y, float2* __restrict__ stats,
+                                                     int T0, T* __restrict__ y, const float2* __restrict__ ss,
                                                      const float* __restrict__ gamma,
                                                      const float* __restrict__ beta, float eps) {
   extern __shared__ float smem[];
@@ -64,7 +68,6 @@ __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pc
   const int nf = min(kChunk, T0 - t0);
   const int nsamp = (nf - 1) * stride + KT;
   float* xs = smem;                                  // [nsamp]
-  float* red = smem + ((nsamp + 3) & ~3);            // [4][C] (group variant)
 
   int vl = valid[b];
   vl = vl < 0 ? 0 : (vl > L ? L : vl);
@@ -129,100 +132,149 @@ __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pc
     return;
   }
 
-  // group variant, pass 1: store the conv output, per-channel sums
-  float sum[kLanesC];
-#pragma unroll
-  for (int c = 0; c < kLanesC; ++c) sum[c] = 0.f;
-  for (int f = wave; f < nf; f += 4) {
-    float v[kLanesC];
-    conv(f, v);
-#pragma unroll
-    for (int c = 0; c < kLanesC; ++c) sum[c] += v[c];
-    if (active) store8<T>(y + ((int64_t)b * T0 + t0 + f) * C + c0, v);
-  }
-  if (active) {
-#pragma unroll
-    for (int c = 0; c < kLanesC; ++c) red[wave * C + c0 + c] = sum[c];
-  }
-  __syncthreads();
-  float mean[kLanesC];
+  // group variant: per-channel scale / shift from gn0_finalize, then GELU
+  float sc[kLanesC], sh[kLanesC];
 #pragma unroll
   for (int c = 0; c < kLanesC; ++c) {
-    mean[c] = active ? (red[c0 + c] + red[C + c0 + c] + red[2 * C + c0 + c] + red[3 * C + c0 + c]) / (float)nf
-                     : 0.f;
+    const float2 p = active ? ss[(int64_t)b * C + c0 + c] : make_float2(0.f, 0.f);
+    sc[c] = p.x;
+    sh[c] = p.y;
   }
-  __syncthreads();
-  // pass 2: centred sum of squares, recomputing the conv from LDS
-  float m2[kLanesC];
-#pragma unroll
-  for (int c = 0; c < kLanesC; ++c) m2[c] = 0.f;
   for (int f = wave; f < nf; f += 4) {
     float v[kLanesC];
     conv(f, v);
 #pragma unroll
-    for (int c = 0; c < kLanesC; ++c) {
-      const float d = v[c] - mean[c];
-      m2[c] = fmaf(d, d, m2[c]);
-    }
+    for (int c = 0; c < kLanesC; ++c) v[c] = gelu_erf(fmaf(v[c], sc[c], sh[c]));
+    if (active) store8<T>(y + ((int64_t)b * T0 + t0 + f) * C + c0, v);
   }
-  if (active) {
-#pragma unroll
-    for (int c = 0; c < kLanesC; ++c) red[wave * C + c0 + c] = m2[c];
+}
+
+// Per (row, chunk of kChunk frames): means of the k shifted sequences and
+// their co-moments (upper triangle, row-major i <= j), in fp64.
+// Output layout per chunk: [mu_0 .. mu_{k-1}, S_00, S_01, .., S_{k-1,k-1}].
+__global__ __launch_bounds__(256) void gn0_stats_kernel(const float* __restrict__ pcm,
+                                                         const int32_t* __restrict__ valid, int L, int k,
+                                                         int stride, int T0, double* __restrict__ part) {
+  extern __shared__ float xs[];  // [(kChunk - 1) * stride + k]
+  __shared__ double mu[16];
+  const int b = blockIdx.y, chunk = blockIdx.x;
+  const int t0 = chunk * kChunk;
+  const int nf = min(kChunk, T0 - t0);
+  const int nsamp = (nf - 1) * stride + k;
+  int vl = valid[b];
+  vl = vl < 0 ? 0 : (vl > L ? L : vl);
+  const int64_t base = (int64_t)t0 * stride;
+  for (int i = threadIdx.x; i < nsamp; i += 256) {
+    const int64_t idx = base + i;
+    xs[i] = (idx < vl) ? pcm[(int64_t)b * L + idx] : 0.f;
   }
   __syncthreads();
-  if (active && wave == 0) {
-    const int nchunk = gridDim.x;
-#pragma unroll
-    for (int c = 0; c < kLanesC; ++c) {
-      const float q = red[c0 + c] + red[C + c0 + c] + red[2 * C + c0 + c] + red[3 * C + c0 + c];
-      stats[((int64_t)b * nchunk + chunk) * C + c0 + c] = make_float2(mean[c], q);
+  const int ns = k + k * (k + 1) / 2;
+  double* out = part + ((int64_t)b * gridDim.x + chunk) * ns;
+  const int tid = threadIdx.x;
+  if (tid < k) {
+    double acc = 0.0;
+    for (int f = 0; f < nf; ++f) acc += (double)xs[f * stride + tid];
+    mu[tid] = acc / nf;
+    out[tid] = acc / nf;
+  }
+  __syncthreads();
+  const int npair = k * (k + 1) / 2;
+  if (tid < npair) {
+    // map tid -> (i, j), i <= j, row-major over the upper triangle
+    int i = 0, rem = tid;
+    while (rem >= k - i) {
+      rem -= k - i;
+      ++i;
     }
+    const int j = i + rem;
+    const double mi = mu[i], mj = mu[j];
+    double acc = 0.0;
+    for (int f = 0; f < nf; ++f) acc += ((double)xs[f * stride + i] - mi) * ((double)xs[f * stride + j] - mj);
+    out[k + tid] = acc;
   }
 }
 
-__global__ void gn_finalize_kernel(const float2* __restrict__ stats, int C, int T0, int nchunk,
-                                   const float* __restrict__ gamma, const float* __restrict__ beta,
-                                   float eps, float2* __restrict__ ss) {
+// One workgroup per row: merge the chunk partials in chunk order with Chan
+// et al.'s pairwise update of the mean vector and the co-moment matrix.
+// Thread e < k(k+1)/2 owns co-moment entry (i, j) and carries its own running
+// copies of mu_i and mu_j (every thread applies the identical update, so the
+// copies agree); threads e < k also carry mu_e.  Output per row:
+// [mu_0 .. mu_{k-1}, S as a full k x k matrix].
+__global__ __launch_bounds__(256) void gn0_merge_kernel(const double* __restrict__ part, int nchunk, int k, int T0,
+                                                         double* __restrict__ merged) {
+  constexpr int kBatch = 16;
+  __shared__ double stage[kBatch * 152];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int ns = k + k * (k + 1) / 2;
+  const int npair = k * (k + 1) / 2;
+  int pi = 0, pj = 0;
+  if (tid < npair) {
+    int rem = tid;
+    while (rem >= k - pi) {
+      rem -= k - pi;
+      ++pi;
+    }
+    pj = pi + rem;
+  }
+  double mi = 0.0, mj = 0.0, me = 0.0, S = 0.0, n = 0.0;
+  const double* src = part + (int64_t)b * nchunk * ns;
+  for (int c0 = 0; c0 < nchunk; c0 += kBatch) {
+    const int nb = min(kBatch, nchunk - c0);
+    __syncthreads();
+    for (int i = tid; i < nb * ns; i += 256) stage[i] = src[(int64_t)c0 * ns + i];
+    __syncthreads();
+    for (int c = 0; c < nb; ++c) {
+      const double* pc = stage + c * ns;
+      const double m = (double)min(kChunk, T0 - (c0 + c) * kChunk);
+      const double nn = n + m;
+      const double f = m / nn;
+      if (tid < npair) {
+        const double di = pc[pi] - mi, dj = pc[pj] - mj;
+        S += pc[k + tid] + di * dj * n * f;
+        mi += di * f;
+        mj += dj * f;
+      }
+      if (tid < k) me += (pc[tid] - me) * f;
+      n = nn;
+    }
+  }
+  double* out = merged + (int64_t)b * (k + k * k);
+  if (tid < k) out[tid] = me;
+  if (tid < npair) {
+    out[k + pi * k + pj] = S;
+    out[k + pj * k + pi] = S;
+  }
+}
+
+// Per (row, channel): mean = w.mu + bias, var = w^T S w / T0, then the affine
+// GroupNorm map folded into scale = gamma * rstd, shift = beta - mean * scale.
+__global__ __launch_bounds__(256) void gn0_finalize_kernel(const double* __restrict__ merged, int k, int T0,
+                                                            const float* __restrict__ w0,
+                                                            const float* __restrict__ bias, int C,
+                                                            const float* __restrict__ gamma,
+                                                            const float* __restrict__ beta, float eps,
+                                                            float2* __restrict__ ss) {
+  __shared__ double st[16 + 16 * 16];
   const int b = blockIdx.y;
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  const double* src = merged + (int64_t)b * (k + k * k);
+  for (int i = threadIdx.x; i < k + k * k; i += 256) st[i] = src[i];
+  __syncthreads();
+  const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= C) return;
-  // Chan et al. pairwise merge of (n, mean, M2), chunks in order
-  double n = 0.0, mean = 0.0, m2 = 0.0;
-  for (int j = 0; j < nchunk; ++j) {
-    const float2 p = stats[((int64_t)b * nchunk + j) * C + c];
-    const double nb = (double)min(kChunk, T0 - j * kChunk);
-    const double nn = n + nb;
-    const double delta = (double)p.x - mean;
-    mean += delta * nb / nn;
-    m2 += (double)p.y + delta * delta * n * nb / nn;
-    n = nn;
+  const float* w = w0 + (int64_t)c * k;
+  double mean = bias ? (double)bias[c] : 0.0, q = 0.0;
+  for (int i = 0; i < k; ++i) {
+    const double wi = (double)w[i];
+    mean += wi * st[i];
+    double r = 0.0;
+    for (int j = 0; j < k; ++j) r += st[k + i * k + j] * (double)w[j];
+    q += wi * r;
   }
-  const double var = m2 / n;
+  const double var = fmax(q / (double)T0, 0.0);
   const float rstd = (float)(1.0 / sqrt(var + (double)eps));
-  const float sc = gamma[c] * rstd;
-  ss[(int64_t)b * C + c] = make_float2(sc, beta[c] - (float)mean * sc);
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void gn_apply_gelu_kernel(T* __restrict__ y, const float2* __restrict__ ss,
-                                                            int T0, int C, int64_t nvec) {
-  constexpr int EPV = 16 / sizeof(T);
-  const int64_t rowel = (int64_t)T0 * C;
-  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec;
-       v += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e = v * EPV;
-    const int b = (int)(e / rowel);
-    const int c = (int)(e % C);
-    const float2* s = ss + (int64_t)b * C + c;
-    uint4 raw = *(const uint4*)(y + e);
-    T* el = (T*)&raw;
-#pragma unroll
-    for (int i = 0; i < EPV; ++i) {
-      const float2 p = s[i];
-      el[i] = (T)gelu_erf(fmaf((float)el[i], p.x, p.y));
-    }
-    *(uint4*)(y + e) = raw;
-  }
+  const float scv = gamma[c] * rstd;
+  ss[(int64_t)b * C + c] = make_float2(scv, beta[c] - (float)mean * scv);
 }
 
 struct ConvChain {
@@ -243,58 +295,59 @@ __global__ void valid_frames_kernel(const int32_t* __restrict__ valid, int B, in
 
 template <typename T, int KT>
 hipError_t conv0_t(const float* pcm, const int32_t* valid, int32_t L, int32_t B, const float* w0,
-                   const float* bias, int32_t C, int32_t k, int32_t stride, int32_t T0, void* y,
-                   float2* stats, const float* gamma, const float* beta, float eps, hipStream_t s) {
+                   const float* bias, int32_t C, int32_t k, int32_t stride, int32_t T0, void* y, const float2* ss,
+                   const float* gamma, const float* beta, float eps, hipStream_t s) {
   const int nchunk = (T0 + kChunk - 1) / kChunk;
   const int nsamp = (kChunk - 1) * stride + KT;
-  const size_t lds = (size_t)(((nsamp + 3) & ~3) + 4 * C) * sizeof(float);
+  const size_t lds = (size_t)((nsamp + 3) & ~3) * sizeof(float);
   hipLaunchKernelGGL((conv0_kernel<T, KT>), dim3(nchunk, B), dim3(256), lds, s, pcm, valid, L, w0, bias,
-                     C, k, stride, T0, (T*)y, stats, gamma, beta, eps);
+                     C, k, stride, T0, (T*)y, ss, gamma, beta, eps);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t conv0_k(int k, const float* pcm, const int32_t* valid, int32_t L, int32_t B, const float* w0,
-                   const float* bias, int32_t C, int32_t stride, int32_t T0, void* y, float2* stats,
+                   const float* bias, int32_t C, int32_t stride, int32_t T0, void* y, const float2* ss,
                    const float* gamma, const float* beta, float eps, hipStream_t s) {
-  if (k == 10) return conv0_t<T, 10>(pcm, valid, L, B, w0, bias, C, k, stride, T0, y, stats, gamma, beta, eps, s);
-  return conv0_t<T, 16>(pcm, valid, L, B, w0, bias, C, k, stride, T0, y, stats, gamma, beta, eps, s);
+  if (k == 10) return conv0_t<T, 10>(pcm, valid, L, B, w0, bias, C, k, stride, T0, y, ss, gamma, beta, eps, s);
+  return conv0_t<T, 16>(pcm, valid, L, B, w0, bias, C, k, stride, T0, y, ss, gamma, beta, eps, s);
 }
 
 }  // namespace
 
-int conv0_chunk_frames() { return kChunk; }
+int64_t gn0_partial_doubles(int32_t k, int32_t T0) {
+  const int64_t nchunk = (T0 + kChunk - 1) / kChunk;
+  // chunk partials, then the merged statistics (k means + k x k co-moments)
+  return nchunk * (k + k * (k + 1) / 2) + k + k * k;
+}
 
 hipError_t launch_conv0(DType t, const float* pcm, const int32_t* valid, int32_t L, int32_t B,
                         const float* w0, const float* bias, int32_t C, int32_t k, int32_t stride,
-                        int32_t T0, void* y, float2* stats, const float* gamma, const float* beta,
+                        int32_t T0, void* y, const float2* ss, const float* gamma, const float* beta,
                         float eps, hipStream_t s) {
   if (t == DType::F16)
-    return conv0_k<half_t>(k, pcm, valid, L, B, w0, bias, C, stride, T0, y, stats, gamma, beta, eps, s);
-  return conv0_k<float>(k, pcm, valid, L, B, w0, bias, C, stride, T0, y, stats, gamma, beta, eps, s);
+    return conv0_k<half_t>(k, pcm, valid, L, B, w0, bias, C, stride, T0, y, ss, gamma, beta, eps, s);
+  return conv0_k<float>(k, pcm, valid, L, B, w0, bias, C, stride, T0, y, ss, gamma, beta, eps, s);
 }
 
-hipError_t launch_gn_finalize(const float2* stats, int32_t B, int32_t C, int32_t T0, int32_t chunk,
-                              const float* gamma, const float* beta, float eps, float2* scale_shift,
-                              hipStream_t s) {
-  (void)chunk;
+hipError_t launch_gn0_stats(const float* pcm, const int32_t* valid, int32_t L, int32_t B, int32_t k, int32_t stride,
+                            int32_t T0, double* part, hipStream_t s) {
   const int nchunk = (T0 + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(gn_finalize_kernel, dim3((C + 255) / 256, B), dim3(256), 0, s, stats, C, T0, nchunk,
-                     gamma, beta, eps, scale_shift);
+  const size_t lds = (size_t)((kChunk - 1) * stride + k) * sizeof(float);
+  hipLaunchKernelGGL(gn0_stats_kernel, dim3(nchunk, B), dim3(256), lds, s, pcm, valid, L, k, stride, T0, part);
   return hipGetLastError();
 }
 
-hipError_t launch_gn_apply_gelu(DType t, void* y, const float2* scale_shift, int32_t B, int32_t T,
-                                int32_t C, hipStream_t s) {
-  const int64_t n = (int64_t)B * T * C;
-  const int epv = t == DType::F16 ? 8 : 4;
-  const int64_t nvec = n / epv;
-  const int64_t want = (nvec + 255) / 256;
-  const int grid = (int)(want < 256 * 64 ? want : 256 * 64);
-  if (t == DType::F16)
-    hipLaunchKernelGGL(gn_apply_gelu_kernel<half_t>, dim3(grid), dim3(256), 0, s, (half_t*)y, scale_shift, T, C, nvec);
-  else
-    hipLaunchKernelGGL(gn_apply_gelu_kernel<float>, dim3(grid), dim3(256), 0, s, (float*)y, scale_shift, T, C, nvec);
+hipError_t launch_gn0_finalize(double* part, int32_t B, int32_t k, int32_t T0, const float* w0, const float* bias,
+                               int32_t C, const float* gamma, const float* beta, float eps, float2* ss,
+                               hipStream_t s) {
+  const int nchunk = (T0 + kChunk - 1) / kChunk;
+  double* merged = part + (int64_t)B * nchunk * (k + k * (k + 1) / 2);
+  hipLaunchKernelGGL(gn0_merge_kernel, dim3(B), dim3(256), 0, s, part, nchunk, k, T0, merged);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gn0_finalize_kernel, dim3((C + 255) / 256, B), dim3(256), 0, s, merged, k, T0, w0, bias, C, gamma,
+                     beta, eps, ss);
   return hipGetLastError();
 }
 

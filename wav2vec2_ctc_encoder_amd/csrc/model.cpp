@@ -10,7 +10,7 @@
 //
 // Data layout in device memory (channels-last throughout):
 //   conv i output        [B, T_i, C_i]   operand type, ping-pong buffers A/B
-//   GroupNorm partials   [B, chunks, C_0] (mean, M2) fp32
+//   GroupNorm partials   [B, chunks, k + k(k+1)/2] fp64 (input lag statistics)
 //   residual stream h    [B*T, d]        fp32
 //   GEMM operand x       [B*T, max(d, C_last)]  operand type (LayerNorm output)
 //   qkv                  [B*T, 3d]       operand type
@@ -204,7 +204,6 @@ struct w2v2_model {
   DType dt = DType::F16;
   int T[W2V2_MAX_CONV] = {};  // frames after conv i
   int Tf = 0;                 // frames per window
-  int nchunk0 = 0;
 
   void* wmem = nullptr;
   size_t wbytes = 0;
@@ -234,7 +233,8 @@ struct w2v2_model {
 
   // workspace regions
   void *bufA = nullptr, *bufB = nullptr;
-  float2 *gn_stats = nullptr, *gn_ss = nullptr;
+  double* gn_part = nullptr;
+  float2* gn_ss = nullptr;
   float* h = nullptr;
   void *x = nullptr, *qkv = nullptr, *attn = nullptr, *ffn = nullptr, *zg = nullptr;
 
@@ -287,14 +287,15 @@ w2v2_status run_frontend(w2v2_model* m, const float* pcm, const int32_t* valid, 
   const DType dt = m->dt;
   const int C0 = c.conv_dim[0];
   if (c.feat_norm == W2V2_NORM_GROUP) {
-    W2V2_LAUNCH(m, s, "conv0_gn_stats",
+    W2V2_LAUNCH(m, s, "gn0_stats",
+                launch_gn0_stats(pcm, valid, c.window, B, c.conv_kernel[0], c.conv_stride[0], m->T[0], m->gn_part, s));
+    W2V2_LAUNCH(m, s, "gn0_finalize",
+                launch_gn0_finalize(m->gn_part, B, c.conv_kernel[0], m->T[0], (const float*)m->conv[0].w,
+                                    m->conv[0].bias, C0, m->conv[0].gamma, m->conv[0].beta, c.eps, m->gn_ss, s));
+    W2V2_LAUNCH(m, s, "conv0_gn_gelu",
                 launch_conv0(dt, pcm, valid, c.window, B, (const float*)m->conv[0].w, m->conv[0].bias, C0,
-                             c.conv_kernel[0], c.conv_stride[0], m->T[0], m->bufA, m->gn_stats, nullptr, nullptr,
+                             c.conv_kernel[0], c.conv_stride[0], m->T[0], m->bufA, m->gn_ss, nullptr, nullptr,
                              c.eps, s));
-    W2V2_LAUNCH(m, s, "gn_finalize",
-                launch_gn_finalize(m->gn_stats, B, C0, m->T[0], conv0_chunk_frames(), m->conv[0].gamma,
-                                   m->conv[0].beta, c.eps, m->gn_ss, s));
-    W2V2_LAUNCH(m, s, "gn_apply_gelu", launch_gn_apply_gelu(dt, m->bufA, m->gn_ss, B, m->T[0], C0, s));
   } else {
     W2V2_LAUNCH(m, s, "conv0_ln_gelu",
                 launch_conv0(dt, pcm, valid, c.window, B, (const float*)m->conv[0].w, m->conv[0].bias, C0,
@@ -524,7 +525,6 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
       m->T[i] = (int)n;
     }
     m->Tf = frames;
-    m->nchunk0 = (m->T[0] + conv0_chunk_frames() - 1) / conv0_chunk_frames();
   }
   const DType dt = m->dt;
   const int d = c.hidden, F = c.ffn, G = c.pos_groups, Cg = d / G, K = c.pos_kernel;
@@ -683,7 +683,7 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
   std::vector<size_t> sizes = {
       (size_t)elA * ds,                                   // bufA
       (size_t)std::max<int64_t>(elB, 1) * ds,             // bufB
-      (size_t)Bm * m->nchunk0 * c.conv_dim[0] * 8,        // gn_stats
+      (size_t)(Bm * gn0_partial_doubles(c.conv_kernel[0], m->T[0]) * 8),  // gn_part
       (size_t)Bm * c.conv_dim[0] * 8,                     // gn_ss
       (size_t)M * d * 4,                                  // h
       (size_t)M * std::max(d, cl) * ds,                   // x
@@ -707,7 +707,7 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
   uint8_t* wsb = (uint8_t*)m->ws;
   m->bufA = wsb + offs[0];
   m->bufB = wsb + offs[1];
-  m->gn_stats = (float2*)(wsb + offs[2]);
+  m->gn_part = (double*)(wsb + offs[2]);
   m->gn_ss = (float2*)(wsb + offs[3]);
   m->h = (float*)(wsb + offs[4]);
   m->x = wsb + offs[5];

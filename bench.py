@@ -35,7 +35,8 @@ PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
-FRONTEND_KERNELS = {"gn0_stats", "gn0_finalize", "conv0_gn_gelu", "conv0_ln_gelu", "conv_gemm", "conv_ln_gelu"}
+FRONTEND_KERNELS = {"gn0_stats", "gn0_finalize", "conv0_gn_gelu", "conv0_ln_gelu", "conv_ln_gelu"} | \
+    {f"conv{i}_gemm" for i in range(1, 8)}
 
 
 def frames(n, ks, ss):
@@ -59,8 +60,8 @@ def algorithmic_work(cfg, B: int, dsize: int) -> dict[str, tuple[str, float]]:
     M = B * Tf
     L = cfg.layers
     w = {}
-    conv_flop = sum(2.0 * B * T[i] * C[i] * cfg.conv_kernel[i] * C[i - 1] for i in range(1, len(C)))
-    w["conv_gemm"] = ("flop", conv_flop)
+    for i in range(1, len(C)):
+        w[f"conv{i}_gemm"] = ("flop", 2.0 * B * T[i] * C[i] * cfg.conv_kernel[i] * C[i - 1])
     if cfg.feat_norm == "group":
         # conv0 + GroupNorm + GELU: read the PCM, write the normalised output once
         w["conv0_gn_gelu"] = ("byte", B * cfg.window * 4.0 + B * T[0] * C[0] * dsize)

@@ -320,7 +320,9 @@ w2v2_status run_frontend(w2v2_model* m, const float* pcm, const int32_t* valid, 
     g.out_t = out;
     g.ldc = c.conv_dim[i];
     g.act = (c.feat_norm == W2V2_NORM_GROUP) ? 1 : 0;
-    W2V2_LAUNCH(m, s, "conv_gemm", launch_gemm(dt, g, s));
+    static const char* kConvName[W2V2_MAX_CONV] = {"conv0",      "conv1_gemm", "conv2_gemm", "conv3_gemm",
+                                                    "conv4_gemm", "conv5_gemm", "conv6_gemm", "conv7_gemm"};
+    W2V2_LAUNCH(m, s, kConvName[i], launch_gemm(dt, g, s));
     if (c.feat_norm == W2V2_NORM_LAYER) {
       W2V2_LAUNCH(m, s, "conv_ln_gelu",
                   launch_layernorm(dt, nullptr, out, (int64_t)B * m->T[i], c.conv_dim[i], m->conv[i].gamma,

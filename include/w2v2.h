@@ -99,7 +99,7 @@ typedef enum { W2V2_FP32 = 0, W2V2_FP16 = 1 } w2v2_precision;
  *
  * Supported limits (else W2V2_E_CONFIG): 1 <= n_conv <= 8, every conv_dim a
  * multiple of 8 in [8, 2048] with conv_dim[0] <= 512, conv_kernel[0] <= 16,
- * conv_stride[0] <= 64, hidden and ffn multiples of 8, hidden <= 2048,
+ * conv_stride[0] <= 8, hidden and ffn multiples of 8, hidden <= 2048,
  * (hidden / pos_groups) a multiple of 8, window long enough for >= 1 frame,
  * at most 16384 frames per window, 1 <= max_batch <= 4096.
  */

@@ -95,6 +95,15 @@ def test_bad_conv_dims_rejected():
     assert st == _lib().E_CONFIG, msg
 
 
+@pytest.mark.parametrize("field,index,value", [("conv_dim", 0, 520), ("conv_kernel", 0, 17),
+                                               ("conv_stride", 0, 9), ("conv_kernel", 3, 0)])
+def test_unsupported_conv0_limits_rejected(field, index, value):
+    cfg, c = _config()
+    getattr(c, field)[index] = value
+    st, _, msg = _create(c, synth.make_weights(cfg))
+    assert st == _lib().E_CONFIG, msg
+
+
 @pytest.mark.parametrize("case", ["empty", "missing", "extra", "duplicate", "shape", "nonfinite"])
 def test_bad_weight_table_rejected(case):
     cfg, c = _config()

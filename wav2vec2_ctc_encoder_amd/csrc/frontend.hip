@@ -27,7 +27,8 @@
 namespace w2v2 {
 namespace {
 
-constexpr int kChunk = 256;  // frames per workgroup
+constexpr int kChunk = 256;       // frames per conv0 workgroup
+constexpr int kStatChunk = 1024;  // frames per GroupNorm-statistics workgroup
 constexpr int kLanesC = 8;   // channels per lane
 
 __device__ inline float wave_sum(float v) {
@@ -149,17 +150,20 @@ __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pc
   }
 }
 
-// Per (row, chunk of kChunk frames): means of the k shifted sequences and
+// Per (row, chunk of kStatChunk frames): means of the k shifted sequences and
 // their co-moments (upper triangle, row-major i <= j), in fp64.
 // Output layout per chunk: [mu_0 .. mu_{k-1}, S_00, S_01, .., S_{k-1,k-1}].
+// Every thread sums a fixed frame-strided share of one quantity; the shares
+// are added in a fixed order, so the result is deterministic.
 __global__ __launch_bounds__(256) void gn0_stats_kernel(const float* __restrict__ pcm,
                                                          const int32_t* __restrict__ valid, int L, int k,
                                                          int stride, int T0, double* __restrict__ part) {
-  extern __shared__ float xs[];  // [(kChunk - 1) * stride + k]
+  extern __shared__ float xs[];  // [(kStatChunk - 1) * stride + k]
+  __shared__ double red[256];
   __shared__ double mu[16];
   const int b = blockIdx.y, chunk = blockIdx.x;
-  const int t0 = chunk * kChunk;
-  const int nf = min(kChunk, T0 - t0);
+  const int t0 = chunk * kStatChunk;
+  const int nf = min(kStatChunk, T0 - t0);
   const int nsamp = (nf - 1) * stride + k;
   int vl = valid[b];
   vl = vl < 0 ? 0 : (vl > L ? L : vl);
@@ -172,26 +176,46 @@ __global__ __launch_bounds__(256) void gn0_stats_kernel(const float* __restrict_
   const int ns = k + k * (k + 1) / 2;
   double* out = part + ((int64_t)b * gridDim.x + chunk) * ns;
   const int tid = threadIdx.x;
+  // means: k quantities x mp shares
+  const int mp = 256 / k;
+  if (tid < k * mp) {
+    const int j = tid % k, sh = tid / k;
+    double acc = 0.0;
+    for (int f = sh; f < nf; f += mp) acc += (double)xs[f * stride + j];
+    red[tid] = acc;
+  }
+  __syncthreads();
   if (tid < k) {
     double acc = 0.0;
-    for (int f = 0; f < nf; ++f) acc += (double)xs[f * stride + tid];
+    for (int sh = 0; sh < mp; ++sh) acc += red[sh * k + tid];
     mu[tid] = acc / nf;
     out[tid] = acc / nf;
   }
   __syncthreads();
+  // co-moments: npair quantities x pp shares
   const int npair = k * (k + 1) / 2;
-  if (tid < npair) {
-    // map tid -> (i, j), i <= j, row-major over the upper triangle
-    int i = 0, rem = tid;
+  const int pp = 256 / npair;
+  double acc = 0.0;
+  int pr = 0;
+  if (tid < npair * pp) {
+    pr = tid % npair;
+    const int sh = tid / npair;
+    int i = 0, rem = pr;
     while (rem >= k - i) {
       rem -= k - i;
       ++i;
     }
     const int j = i + rem;
     const double mi = mu[i], mj = mu[j];
-    double acc = 0.0;
-    for (int f = 0; f < nf; ++f) acc += ((double)xs[f * stride + i] - mi) * ((double)xs[f * stride + j] - mj);
-    out[k + tid] = acc;
+    for (int f = sh; f < nf; f += pp) acc += ((double)xs[f * stride + i] - mi) * ((double)xs[f * stride + j] - mj);
+  }
+  __syncthreads();
+  if (tid < npair * pp) red[tid] = acc;
+  __syncthreads();
+  if (tid < npair) {
+    double tot = 0.0;
+    for (int sh = 0; sh < pp; ++sh) tot += red[sh * npair + tid];
+    out[k + tid] = tot;
   }
 }
 
@@ -226,7 +250,7 @@ __global__ __launch_bounds__(256) void gn0_merge_kernel(const double* __restrict
     __syncthreads();
     for (int c = 0; c < nb; ++c) {
       const double* pc = stage + c * ns;
-      const double m = (double)min(kChunk, T0 - (c0 + c) * kChunk);
+      const double m = (double)min(kStatChunk, T0 - (c0 + c) * kStatChunk);
       const double nn = n + m;
       const double f = m / nn;
       if (tid < npair) {
@@ -316,7 +340,7 @@ hipError_t conv0_k(int k, const float* pcm, const int32_t* valid, int32_t L, int
 }  // namespace
 
 int64_t gn0_partial_doubles(int32_t k, int32_t T0) {
-  const int64_t nchunk = (T0 + kChunk - 1) / kChunk;
+  const int64_t nchunk = (T0 + kStatChunk - 1) / kStatChunk;
   // chunk partials, then the merged statistics (k means + k x k co-moments)
   return nchunk * (k + k * (k + 1) / 2) + k + k * k;
 }
@@ -332,8 +356,8 @@ hipError_t launch_conv0(DType t, const float* pcm, const int32_t* valid, int32_t
 
 hipError_t launch_gn0_stats(const float* pcm, const int32_t* valid, int32_t L, int32_t B, int32_t k, int32_t stride,
                             int32_t T0, double* part, hipStream_t s) {
-  const int nchunk = (T0 + kChunk - 1) / kChunk;
-  const size_t lds = (size_t)((kChunk - 1) * stride + k) * sizeof(float);
+  const int nchunk = (T0 + kStatChunk - 1) / kStatChunk;
+  const size_t lds = (size_t)((kStatChunk - 1) * stride + k) * sizeof(float);
   hipLaunchKernelGGL(gn0_stats_kernel, dim3(nchunk, B), dim3(256), lds, s, pcm, valid, L, k, stride, T0, part);
   return hipGetLastError();
 }
@@ -341,7 +365,7 @@ hipError_t launch_gn0_stats(const float* pcm, const int32_t* valid, int32_t L, i
 hipError_t launch_gn0_finalize(double* part, int32_t B, int32_t k, int32_t T0, const float* w0, const float* bias,
                                int32_t C, const float* gamma, const float* beta, float eps, float2* ss,
                                hipStream_t s) {
-  const int nchunk = (T0 + kChunk - 1) / kChunk;
+  const int nchunk = (T0 + kStatChunk - 1) / kStatChunk;
   double* merged = part + (int64_t)B * nchunk * (k + k * (k + 1) / 2);
   hipLaunchKernelGGL(gn0_merge_kernel, dim3(B), dim3(256), 0, s, part, nchunk, k, T0, merged);
   hipError_t e = hipGetLastError();

@@ -420,7 +420,30 @@ __device__ inline void dma16(const void* gptr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int BKB, int ROLE>
+// s_waitcnt vmcnt(LPS * ahead) for a run-time ahead in [0, MAXA]; the count
+// is an instruction immediate, so each case is its own instruction.
+// Encoding (gfx9): vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8];
+// expcnt / lgkmcnt are left at their maxima (no wait).
+template <int N>
+__device__ inline void wait_vmcnt_imm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+template <int LPS, int MAXA>
+__device__ inline void wait_vmcnt_steps(int ahead) {
+  if constexpr (MAXA >= 3) {
+    if (ahead >= 3) { wait_vmcnt_imm<LPS * 3>(); return; }
+  }
+  if constexpr (MAXA >= 2) {
+    if (ahead == 2) { wait_vmcnt_imm<LPS * 2>(); return; }
+  }
+  if constexpr (MAXA >= 1) {
+    if (ahead == 1) { wait_vmcnt_imm<LPS>(); return; }
+  }
+  wait_vmcnt_imm<0>();
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, int BKB, int ROLE, int SCHED = 0>
 __global__ __launch_bounds__(256, 1) void gemm_dlds_kernel(GemmArgs a) {
   constexpr int TM = BM / WM / 32;
   constexpr int TN = BN / WN / 32;
@@ -432,7 +455,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dlds_kernel(GemmArgs a) {
   constexpr int JB = BN / RPI / 4;       // (B)
   constexpr int LPS = JA + JB;           // loads per thread per stage
   static_assert(WM * WN == 4 && TM >= 1 && TN >= 1, "4 waves");
-  static_assert(JA >= 1 && JB >= 1 && LPS <= 15, "tile / vmcnt range");
+  static_assert(JA >= 1 && JB >= 1 && LPS * (STAGES - 2) <= 63 && STAGES <= 5, "tile / vmcnt range");
 
   __shared__ uint4 sA[STAGES][BM * CPR];
   __shared__ uint4 sB[STAGES][BN * CPR];
@@ -519,11 +542,12 @@ __global__ __launch_bounds__(256, 1) void gemm_dlds_kernel(GemmArgs a) {
   }
 
   for (int kt = 0; kt < nk; ++kt) {
-    // wait for this step's loads (later steps may stay in flight), publish
-    if (kt + 1 < nk && STAGES > 2)
-      __builtin_amdgcn_s_waitcnt((LPS & 0xF) | ((LPS >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-    else
-      __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
+    // wait for this step's loads while the later steps already issued
+    // (min(STAGES - 2, nk - 1 - kt) of them, LPS loads each) stay in flight;
+    // vector-memory loads retire in order, so vmcnt(n) leaves the newest n
+    // outstanding.  Then publish the step to the whole workgroup.
+    const int ahead = min(STAGES - 2, nk - 1 - kt);
+    wait_vmcnt_steps<LPS, STAGES - 2>(ahead);
     __builtin_amdgcn_s_barrier();
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
     const int buf = kt % STAGES;
@@ -549,6 +573,14 @@ __global__ __launch_bounds__(256, 1) void gemm_dlds_kernel(GemmArgs a) {
         for (int j = 0; j < TM; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, wv[cur][i]),
                                                              __builtin_bit_cast(h8, av[cur][j]), acc[i][j], 0, 0, 0);
+    }
+    if constexpr (SCHED == 1) {
+      // interleave: one MFMA, then the LDS fragment reads that fit under it
+#pragma unroll
+      for (int i = 0; i < TM * TN * KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
     // all LDS reads of this buffer have been consumed by the MFMAs above;
     // make sure they completed before the next barrier lets the buffer refill
@@ -587,7 +619,8 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
 template <int BM, int BN, int ST, int BKB, int ROLE>
 hipError_t launch_dlds(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_dlds_kernel<BM, BN, 2, 2, ST, BKB, ROLE>), dim3(tiles, 1, a.groups), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_dlds_kernel<BM, BN, 2, 2, ST, BKB, ROLE, 1>), dim3(tiles, 1, a.groups), dim3(256), 0, s,
+                     a);
   return hipGetLastError();
 }
 
@@ -597,9 +630,10 @@ hipError_t launch_shape(const GemmArgs& a, hipStream_t s) {
     // direct-to-LDS pipeline: whole 64-wide K steps, N wide enough to fill a tile
     if (a.K % 64 == 0 && a.N > 32) {
       const int64_t tiles128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.groups;
-      // 128x128 tiles are the most efficient per flop; with fewer than four
-      // rounds of two tiles per CU, 128x64 tiles balance the CUs better.
-      if (a.N > 64 && tiles128 >= 1024) return launch_dlds<128, 128, 2, 128, ROLE>(a, s);
+      // 128x128 tiles win on the long conv GEMMs; below ~3 rounds of two
+      // tiles per CU, 128x64 tiles balance the CUs better (measured on the
+      // encoder shapes M = 6392, N = 768..3072).
+      if (a.N > 64 && tiles128 >= 1536) return launch_dlds<128, 128, 2, 128, ROLE>(a, s);
       return launch_dlds<128, 64, 2, 128, ROLE>(a, s);
     }
   }

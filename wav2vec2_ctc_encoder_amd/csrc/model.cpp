@@ -114,7 +114,7 @@ std::string check_config(const w2v2_config& c, int* frames_out) {
   }
   if (c.conv_dim[0] > 512) return bad("conv_dim[0] must be <= 512");
   if (c.conv_kernel[0] > 16) return bad("conv_kernel[0] must be <= 16");
-  if (c.conv_stride[0] > 64) return bad("conv_stride[0] must be <= 64");
+  if (c.conv_stride[0] > 8) return bad("conv_stride[0] must be <= 8");
   if (c.conv_bias != 0 && c.conv_bias != 1) return bad("conv_bias must be 0 or 1");
   if (c.feat_norm != W2V2_NORM_GROUP && c.feat_norm != W2V2_NORM_LAYER) return bad("unknown feat_norm");
   if (c.hidden < 8 || c.hidden > 2048 || c.hidden % 8) return bad("hidden must be a multiple of 8 in [8, 2048]");

@@ -65,6 +65,7 @@ typedef enum {
 
 typedef enum { W2V2_NORM_GROUP = 0, W2V2_NORM_LAYER = 1 } w2v2_feat_norm;
 typedef enum { W2V2_FP32 = 0, W2V2_FP16 = 1 } w2v2_precision;
+typedef enum { W2V2_GELU_ERF = 0, W2V2_GELU_TANH = 1 } w2v2_gelu;
 
 /*
  * Network shape and workload limits.  The fields mirror the checkpoint config
@@ -96,6 +97,11 @@ typedef enum { W2V2_FP32 = 0, W2V2_FP16 = 1 } w2v2_precision;
  *  max_batch       largest batch a forward call may pass (workspace size).
  *  window          samples per PCM window (fixed per model, [LiteRT]
  *                  "Rewrites for the GPU").
+ *  gelu_kind       W2V2_GELU_ERF: exact GELU x/2 (1 + erf(x / sqrt 2)) at every
+ *                  GELU of the network (default).  W2V2_GELU_TANH: the tanh
+ *                  approximation x/2 (1 + tanh(sqrt(2/pi)(x + 0.044715 x^3)))
+ *                  everywhere, for parity with graphs exported that way
+ *                  ([LiteRT] "Rewrites for the GPU": GELU -> tanh-GELU).
  *
  * Supported limits (else W2V2_E_CONFIG): 1 <= n_conv <= 8, every conv_dim a
  * multiple of 8 in [8, 2048] with conv_dim[0] <= 512, conv_kernel[0] <= 16,
@@ -124,6 +130,7 @@ typedef struct {
   int32_t precision;
   int32_t max_batch;
   int32_t window;
+  int32_t gelu_kind;
 } w2v2_config;
 
 /*

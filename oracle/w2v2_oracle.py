@@ -48,6 +48,21 @@ def gelu(x: np.ndarray) -> np.ndarray:
     return 0.5 * x * (1.0 + _erf(x / np.sqrt(x.dtype.type(2.0))))
 
 
+def gelu_tanh(x: np.ndarray) -> np.ndarray:
+    """tanh approximation of GELU, x/2 * (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+    (Hendrycks & Gimpel).  The LiteRT discussion ("Rewrites for the GPU")
+    exports the model with this form because the mobile GPU rejects erf; it
+    is the compatibility option of the network, not its default."""
+    x = np.asarray(x)
+    c = np.sqrt(x.dtype.type(2.0) / x.dtype.type(np.pi))
+    return 0.5 * x * (1.0 + np.tanh(c * (x + 0.044715 * x ** 3)))
+
+
+def activation(cfg):
+    """The GELU flavour a config selects (exact erf unless gelu == "tanh")."""
+    return gelu_tanh if getattr(cfg, "gelu", "erf") == "tanh" else gelu
+
+
 def layer_norm(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float,
                axis: int = -1) -> np.ndarray:
     """LayerNorm over ``axis``: biased variance, eps inside the square root."""
@@ -177,12 +192,13 @@ def self_attention(h: np.ndarray, W: dict, prefix: str, heads: int) -> np.ndarra
     return proj("out", o)
 
 
-def feed_forward(h: np.ndarray, W: dict, prefix: str) -> np.ndarray:
+def feed_forward(h: np.ndarray, W: dict, prefix: str, act=None) -> np.ndarray:
     """fc2(GELU(fc1(h))), both linears with bias (TensorRT README, "Recipe that
     was measured": intermediate_dense and output_dense)."""
     dt = h.dtype
+    act = gelu if act is None else act
     u = np.matmul(h, W[prefix + "fc1.weight"].astype(dt).T) + W[prefix + "fc1.bias"].astype(dt)
-    return np.matmul(gelu(u), W[prefix + "fc2.weight"].astype(dt).T) + W[prefix + "fc2.bias"].astype(dt)
+    return np.matmul(act(u), W[prefix + "fc2.weight"].astype(dt).T) + W[prefix + "fc2.bias"].astype(dt)
 
 
 # ----------------------------------------------------------------------------
@@ -211,6 +227,7 @@ def feature_encoder(cfg, W: dict, pcm: np.ndarray, valid: np.ndarray,
       layer-normalized feature encoders, with or without convolution bias).
     """
     dt = np.dtype(dtype)
+    act = activation(cfg)
     x = np.asarray(pcm, dtype=dt).copy()
     for b in range(x.shape[0]):
         x[b, int(valid[b]):] = 0.0
@@ -225,7 +242,7 @@ def feature_encoder(cfg, W: dict, pcm: np.ndarray, valid: np.ndarray,
         elif i == 0:
             h = group_norm_over_time(h, W["fe.norm0.weight"].astype(dt), W["fe.norm0.bias"].astype(dt),
                                      cfg.eps)
-        h = gelu(h)
+        h = act(h)
     return h
 
 
@@ -234,6 +251,9 @@ def encoder(cfg, W: dict, feats: np.ndarray) -> np.ndarray:
 
     feats [B, C, T] -> hidden [B, T, d].
 
+    * GELU is the exact erf form unless the config selects the tanh
+      approximation (compatibility with the tanh-GELU export of the LiteRT
+      discussion, "Rewrites for the GPU").
     * Feature projection: LayerNorm over C per frame, then Linear C -> d.
     * Positional conv: h = z + GELU(posconv(z)), with the weight norm folded
       from (v, g) on every call (LiteRT discussion, "Rewrites for the GPU").
@@ -247,6 +267,7 @@ def encoder(cfg, W: dict, feats: np.ndarray) -> np.ndarray:
     """
     dt = feats.dtype
     eps = cfg.eps
+    act = activation(cfg)
 
     def g(name):
         return W[name].astype(dt)
@@ -255,7 +276,7 @@ def encoder(cfg, W: dict, feats: np.ndarray) -> np.ndarray:
     f = layer_norm(f, g("fp.norm.weight"), g("fp.norm.bias"), eps)
     z = np.matmul(f, g("fp.proj.weight").T) + g("fp.proj.bias")
     w_pos = fold_weight_norm(g("pos.weight_v"), g("pos.weight_g"))
-    h = z + gelu(positional_conv(z, w_pos, g("pos.bias"), cfg.pos_groups))
+    h = z + act(positional_conv(z, w_pos, g("pos.bias"), cfg.pos_groups))
     if not cfg.stable_layer_norm:
         h = layer_norm(h, g("enc.norm.weight"), g("enc.norm.bias"), eps)
     for l in range(cfg.layers):
@@ -264,11 +285,11 @@ def encoder(cfg, W: dict, feats: np.ndarray) -> np.ndarray:
             a = layer_norm(h, g(p + "attn_norm.weight"), g(p + "attn_norm.bias"), eps)
             h = h + self_attention(a, W, p + "attn.", cfg.heads)
             a = layer_norm(h, g(p + "ffn_norm.weight"), g(p + "ffn_norm.bias"), eps)
-            h = h + feed_forward(a, W, p + "ffn.")
+            h = h + feed_forward(a, W, p + "ffn.", act)
         else:
             h = layer_norm(h + self_attention(h, W, p + "attn.", cfg.heads),
                            g(p + "attn_norm.weight"), g(p + "attn_norm.bias"), eps)
-            h = layer_norm(h + feed_forward(h, W, p + "ffn."),
+            h = layer_norm(h + feed_forward(h, W, p + "ffn.", act),
                            g(p + "ffn_norm.weight"), g(p + "ffn_norm.bias"), eps)
     if cfg.stable_layer_norm:
         h = layer_norm(h, g("enc.norm.weight"), g("enc.norm.bias"), eps)

@@ -52,6 +52,7 @@ class W2V2Config:
     vocab: int = 32
     blank_id: int = 0
     eps: float = 1e-5
+    gelu: str = "erf"                 # "erf" (exact) | "tanh" (tanh approximation)
     precision: str = "fp16"           # "fp32" | "fp16" (fp16 operands, fp32 accumulate/normalise)
     window: int = 256000              # samples per window
     batch: int = 8

@@ -77,6 +77,7 @@ def _create(cfg_struct, weights):
     ("abi_version", 99), ("n_conv", 0), ("n_conv", 9), ("heads", 5), ("heads", 64), ("ffn", 12),
     ("pos_groups", 3), ("vocab", 0), ("blank_id", 32), ("blank_id", -1), ("eps", 0.0),
     ("precision", 7), ("max_batch", 0), ("max_batch", 5000), ("window", 399), ("feat_norm", 3),
+    ("gelu_kind", 2),
 ])
 def test_bad_config_rejected_before_device_work(field, value):
     cfg, c = _config()

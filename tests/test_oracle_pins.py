@@ -165,6 +165,21 @@ def test_gelu_vs_math_erf():
     np.testing.assert_allclose(oracle.gelu(np.array(1.0)), 0.8413447460685429, rtol=1e-15)
 
 
+def test_gelu_tanh_matches_torch_tanh_approximation():
+    torch = pytest.importorskip("torch")
+    xs = np.linspace(-10, 10, 2001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(xs), approximate="tanh").numpy()
+    np.testing.assert_allclose(oracle.gelu_tanh(xs), ref, rtol=1e-13, atol=1e-15)
+    assert oracle.gelu_tanh(np.array(0.0)) == 0.0
+    # the approximation stays within 5e-4 of the exact form (Hendrycks & Gimpel)
+    assert np.abs(oracle.gelu_tanh(xs) - oracle.gelu(xs)).max() < 5e-4
+
+
+def test_activation_follows_config():
+    assert oracle.activation(_tiny()) is oracle.gelu
+    assert oracle.activation(_tiny(gelu="tanh")) is oracle.gelu_tanh
+
+
 # ----------------------------------------------------------------------------
 # weight norm and positional conv
 # ----------------------------------------------------------------------------
@@ -440,7 +455,8 @@ def _hf_logits(cfg, W, pcm):
         conv_kernel=cfg.conv_kernel, conv_stride=cfg.conv_stride, conv_bias=cfg.conv_bias,
         num_conv_pos_embeddings=cfg.pos_kernel, num_conv_pos_embedding_groups=cfg.pos_groups,
         feat_extract_norm=cfg.feat_norm, do_stable_layer_norm=cfg.stable_layer_norm,
-        hidden_act="gelu", feat_extract_activation="gelu", layer_norm_eps=cfg.eps,
+        hidden_act="gelu_new" if cfg.gelu == "tanh" else "gelu",
+        feat_extract_activation="gelu_new" if cfg.gelu == "tanh" else "gelu", layer_norm_eps=cfg.eps,
         pad_token_id=cfg.blank_id)
     torch.manual_seed(0)
     model = tr.Wav2Vec2ForCTC(hc).double().eval()
@@ -461,6 +477,7 @@ _VARIANTS = {
     "group_postnorm": dict(),
     "layer_stable": dict(feat_norm="layer", conv_bias=True, stable_layer_norm=True),
     "group_postnorm_odd_pos_kernel": dict(pos_kernel=15),
+    "layer_stable_tanh_gelu": dict(feat_norm="layer", conv_bias=True, stable_layer_norm=True, gelu="tanh"),
 }
 
 

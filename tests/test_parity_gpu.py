@@ -123,6 +123,8 @@ _TINY_VARIANTS = {
     "head32_window_tail": _TINY.replace(hidden=128, heads=4, window=16000 + 3333, batch=2,
                                         valid_range=(9000, 19333)),
     "head128": _TINY.replace(hidden=256, heads=2, ffn=512, pos_groups=8),
+    "tanh_gelu_group": _TINY.replace(gelu="tanh", batch=2, valid_range=(8000, 16000)),
+    "tanh_gelu_layer_stable": _TINY.replace(gelu="tanh", feat_norm="layer", conv_bias=True, stable_layer_norm=True),
 }
 
 
@@ -148,6 +150,37 @@ def test_tiny_fp16_correlates(variant):
     _say(f"pearson {r:.6f}")
     assert r >= 0.999
     _check_ids(cfg, logits, vf, ids, lens)
+
+
+def test_tanh_gelu_mode_on_base_shape():
+    """The tanh-GELU compatibility mode at the base 10 s shape in fp16 meets
+    the fp16 gates against the tanh-GELU oracle, and its deviation from the
+    exact-GELU network is reported."""
+    cfg = synth.BASE_10S_B1.replace(gelu="tanh", window=96000)
+    _say("base 6 s tanh-GELU fp16")
+    ref, vf_ref = _oracle(cfg, (0,))
+    logits, vf, ids, lens = _gpu_forward(cfg, precision="fp16")
+    _gate_fp16(logits, ref, vf_ref)
+    ref_erf, _ = _oracle(cfg.replace(gelu="erf"), (0,))
+    _say(f"tanh-vs-erf network: max-abs {np.abs(ref - ref_erf).max():.3e}, "
+         f"pearson {_pearson(ref, ref_erf):.6f}, "
+         f"argmax agreement {np.mean(np.argmax(ref[0, :vf_ref[0]], -1) == np.argmax(ref_erf[0, :vf_ref[0]], -1)):.4f}")
+
+
+@pytest.mark.parametrize("dc", [0.5, -2.0])
+def test_dc_offset_pcm(dc):
+    """GroupNorm statistics under a large DC offset (the variance is small
+    next to the mean): fp32 gate against the oracle."""
+    import wav2vec2_ctc_encoder_amd as w2
+    cfg = _TINY.replace(batch=2, valid_range=(12000, 16000))
+    _say(f"pcm + DC {dc}")
+    W, pcm, valid = _inputs(cfg)
+    pcm = pcm.copy()
+    for b in range(cfg.batch):
+        pcm[b, :valid[b]] += np.float32(dc)
+    ref, vf_ref = oracle.forward(cfg, W, pcm, valid)
+    logits, vf, ids, lens = _gpu_forward(cfg, precision="fp32", pcm=pcm, valid=valid)
+    _gate_fp32(logits, ref)
 
 
 def test_samples_beyond_valid_are_ignored():

@@ -35,7 +35,7 @@ def make_config(cfg: Any, max_batch: int | None = None, precision: str | None = 
     ``w2v2_config`` (conv_dim, conv_kernel, conv_stride, conv_bias,
     feat_norm "group"/"layer", hidden, heads, ffn, layers, pos_kernel,
     pos_groups, stable_layer_norm, vocab, blank_id, eps, precision
-    "fp32"/"fp16", window, batch)."""
+    "fp32"/"fp16", window, batch, gelu "erf"/"tanh")."""
     c = _lib.Config()
     c.abi_version = _lib.ABI_VERSION
     dims, ks, ss = list(_get(cfg, "conv_dim")), list(_get(cfg, "conv_kernel")), list(_get(cfg, "conv_stride"))
@@ -56,6 +56,8 @@ def make_config(cfg: Any, max_batch: int | None = None, precision: str | None = 
     c.precision = {"fp32": 0, "fp16": 1}[prec] if isinstance(prec, str) else int(prec)
     c.max_batch = int(max_batch if max_batch is not None else _get(cfg, "batch", 1))
     c.window = int(_get(cfg, "window"))
+    g = _get(cfg, "gelu", "erf")
+    c.gelu_kind = {"erf": 0, "tanh": 1}[g] if isinstance(g, str) else int(g)
     return c
 
 

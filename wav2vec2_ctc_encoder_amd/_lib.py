@@ -44,6 +44,7 @@ class Config(ctypes.Structure):
         ("precision", ctypes.c_int32),
         ("max_batch", ctypes.c_int32),
         ("window", ctypes.c_int32),
+        ("gelu_kind", ctypes.c_int32),
     ]
 
 

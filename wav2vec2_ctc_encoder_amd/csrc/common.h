@@ -35,6 +35,24 @@ __device__ inline float gelu_erf(float x) {
   return x >= 0.f ? x - h : h;
 }
 
+// tanh approximation of GELU, x/2 (1 + tanh(u)) with u = sqrt(2/pi)(x +
+// 0.044715 x^3) (Hendrycks & Gimpel), written as x * sigmoid(2u) =
+// x / (1 + exp(-2u)): saturates cleanly to x and to -0 for large |x|.
+__device__ inline float gelu_tanh(float x) {
+  const float u = 0.7978845608028654f * fmaf(0.044715f * x, x * x, x);
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.8853900817779268f * u));  // 2 log2(e) u
+}
+
+// Activation codes of the kernels: 0 none, 1 erf GELU, 2 tanh GELU.  Hot
+// loops take the code as a template argument (selected once per launch) so
+// that only one form is compiled into them.
+template <int ACT>
+__device__ inline float act_fn(float x) {
+  if constexpr (ACT == 1) return gelu_erf(x);
+  else if constexpr (ACT == 2) return gelu_tanh(x);
+  else return x;
+}
+
 // Kernel-timing hook of the runtime: called around every launch.
 struct LaunchHook {
   virtual void before(const char* name, hipStream_t s) = 0;
@@ -74,7 +92,7 @@ struct GemmArgs {
   float* out_f32 = nullptr;
   void* out_t = nullptr;
   int64_t ldc = 0, c_group = 0;
-  int32_t act = 0;  // 0 none, 1 exact GELU
+  int32_t act = 0;  // 0 none, 1 erf GELU, 2 tanh GELU (applied after the bias)
 };
 
 // Tile shape is chosen from N: 128x32, 128x48, 128x64 or 128x128.
@@ -93,7 +111,7 @@ hipError_t launch_gemm(DType t, const GemmArgs& a, hipStream_t s);
 hipError_t launch_conv0(DType t, const float* pcm, const int32_t* valid, int32_t L, int32_t B,
                         const float* w0, const float* bias, int32_t C, int32_t k, int32_t stride,
                         int32_t T0, void* y, const float2* ss, const float* gamma, const float* beta,
-                        float eps, hipStream_t s);
+                        float eps, int32_t act, hipStream_t s);
 // GroupNorm statistics of conv 0 from the PCM alone: per-chunk means and
 // co-moments of the k shifted sample sequences (fp64), then per (b, c)
 // scale = gamma * rstd and shift = beta - mean * scale.
@@ -111,7 +129,8 @@ hipError_t launch_gn0_finalize(double* part, int32_t B, int32_t k, int32_t T0, c
 // ----------------------------------------------------------------------------
 // LayerNorm over the C entries of each of R rows.  Input fp32 (x_f32) or the
 // operand type (x_t); outputs fp32 (y_f32) and/or operand type (y_t); act 1
-// applies exact GELU after the affine map.  Input and output may alias.
+// (erf GELU) or 2 (tanh GELU) is applied after the affine map.  Input and
+// output may alias.
 hipError_t launch_layernorm(DType t, const float* x_f32, const void* x_t, int64_t R, int32_t C,
                             const float* gamma, const float* beta, float eps, float* y_f32,
                             void* y_t, int32_t act, hipStream_t s);

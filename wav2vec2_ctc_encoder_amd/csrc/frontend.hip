@@ -31,6 +31,11 @@ constexpr int kChunk = 256;       // frames per conv0 workgroup
 constexpr int kStatChunk = 1024;  // frames per GroupNorm-statistics workgroup
 constexpr int kLanesC = 8;   // channels per lane
 
+template <int N>
+struct ActTag {
+  static constexpr int value = N;
+};
+
 __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -61,7 +66,7 @@ __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pc
                                                      const float* __restrict__ bias, int C, int k, int stride,
                                                      int T0, T* __restrict__ y, const float2* __restrict__ ss,
                                                      const float* __restrict__ gamma,
-                                                     const float* __restrict__ beta, float eps) {
+                                                     const float* __restrict__ beta, float eps, int act) {
   extern __shared__ float smem[];
   const int b = blockIdx.y;
   const int chunk = blockIdx.x;
@@ -112,24 +117,29 @@ __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pc
       be[c] = active ? beta[c0 + c] : 0.f;
     }
     const float invC = 1.f / (float)C;
-    for (int f = wave; f < nf; f += 4) {
-      float v[kLanesC];
-      conv(f, v);
-      float s = 0.f;
+    auto frames = [&](auto act_tag) {
+      constexpr int ACT = decltype(act_tag)::value;
+      for (int f = wave; f < nf; f += 4) {
+        float v[kLanesC];
+        conv(f, v);
+        float s = 0.f;
 #pragma unroll
-      for (int c = 0; c < kLanesC; ++c) s += active ? v[c] : 0.f;
-      const float mean = wave_sum(s) * invC;
-      float q = 0.f;
+        for (int c = 0; c < kLanesC; ++c) s += active ? v[c] : 0.f;
+        const float mean = wave_sum(s) * invC;
+        float q = 0.f;
 #pragma unroll
-      for (int c = 0; c < kLanesC; ++c) {
-        const float d = v[c] - mean;
-        q += active ? d * d : 0.f;
+        for (int c = 0; c < kLanesC; ++c) {
+          const float d = v[c] - mean;
+          q += active ? d * d : 0.f;
+        }
+        const float rstd = rsqrtf(wave_sum(q) * invC + eps);
+#pragma unroll
+        for (int c = 0; c < kLanesC; ++c) v[c] = act_fn<ACT>((v[c] - mean) * rstd * g[c] + be[c]);
+        if (active) store8<T>(y + ((int64_t)b * T0 + t0 + f) * C + c0, v);
       }
-      const float rstd = rsqrtf(wave_sum(q) * invC + eps);
-#pragma unroll
-      for (int c = 0; c < kLanesC; ++c) v[c] = gelu_erf((v[c] - mean) * rstd * g[c] + be[c]);
-      if (active) store8<T>(y + ((int64_t)b * T0 + t0 + f) * C + c0, v);
-    }
+    };
+    if (act == 2) frames(ActTag<2>{});
+    else frames(ActTag<1>{});
     return;
   }
 
@@ -141,13 +151,18 @@ __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pc
     sc[c] = p.x;
     sh[c] = p.y;
   }
-  for (int f = wave; f < nf; f += 4) {
-    float v[kLanesC];
-    conv(f, v);
+  auto frames = [&](auto act_tag) {
+    constexpr int ACT = decltype(act_tag)::value;
+    for (int f = wave; f < nf; f += 4) {
+      float v[kLanesC];
+      conv(f, v);
 #pragma unroll
-    for (int c = 0; c < kLanesC; ++c) v[c] = gelu_erf(fmaf(v[c], sc[c], sh[c]));
-    if (active) store8<T>(y + ((int64_t)b * T0 + t0 + f) * C + c0, v);
-  }
+      for (int c = 0; c < kLanesC; ++c) v[c] = act_fn<ACT>(fmaf(v[c], sc[c], sh[c]));
+      if (active) store8<T>(y + ((int64_t)b * T0 + t0 + f) * C + c0, v);
+    }
+  };
+  if (act == 2) frames(ActTag<2>{});
+  else frames(ActTag<1>{});
 }
 
 // Per (row, chunk of kStatChunk frames): means of the k shifted sequences and
@@ -320,21 +335,21 @@ __global__ void valid_frames_kernel(const int32_t* __restrict__ valid, int B, in
 template <typename T, int KT>
 hipError_t conv0_t(const float* pcm, const int32_t* valid, int32_t L, int32_t B, const float* w0,
                    const float* bias, int32_t C, int32_t k, int32_t stride, int32_t T0, void* y, const float2* ss,
-                   const float* gamma, const float* beta, float eps, hipStream_t s) {
+                   const float* gamma, const float* beta, float eps, int32_t act, hipStream_t s) {
   const int nchunk = (T0 + kChunk - 1) / kChunk;
   const int nsamp = (kChunk - 1) * stride + KT;
   const size_t lds = (size_t)((nsamp + 3) & ~3) * sizeof(float);
   hipLaunchKernelGGL((conv0_kernel<T, KT>), dim3(nchunk, B), dim3(256), lds, s, pcm, valid, L, w0, bias,
-                     C, k, stride, T0, (T*)y, ss, gamma, beta, eps);
+                     C, k, stride, T0, (T*)y, ss, gamma, beta, eps, act);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t conv0_k(int k, const float* pcm, const int32_t* valid, int32_t L, int32_t B, const float* w0,
                    const float* bias, int32_t C, int32_t stride, int32_t T0, void* y, const float2* ss,
-                   const float* gamma, const float* beta, float eps, hipStream_t s) {
-  if (k == 10) return conv0_t<T, 10>(pcm, valid, L, B, w0, bias, C, k, stride, T0, y, ss, gamma, beta, eps, s);
-  return conv0_t<T, 16>(pcm, valid, L, B, w0, bias, C, k, stride, T0, y, ss, gamma, beta, eps, s);
+                   const float* gamma, const float* beta, float eps, int32_t act, hipStream_t s) {
+  if (k == 10) return conv0_t<T, 10>(pcm, valid, L, B, w0, bias, C, k, stride, T0, y, ss, gamma, beta, eps, act, s);
+  return conv0_t<T, 16>(pcm, valid, L, B, w0, bias, C, k, stride, T0, y, ss, gamma, beta, eps, act, s);
 }
 
 }  // namespace
@@ -348,10 +363,10 @@ int64_t gn0_partial_doubles(int32_t k, int32_t T0) {
 hipError_t launch_conv0(DType t, const float* pcm, const int32_t* valid, int32_t L, int32_t B,
                         const float* w0, const float* bias, int32_t C, int32_t k, int32_t stride,
                         int32_t T0, void* y, const float2* ss, const float* gamma, const float* beta,
-                        float eps, hipStream_t s) {
+                        float eps, int32_t act, hipStream_t s) {
   if (t == DType::F16)
-    return conv0_k<half_t>(k, pcm, valid, L, B, w0, bias, C, stride, T0, y, ss, gamma, beta, eps, s);
-  return conv0_k<float>(k, pcm, valid, L, B, w0, bias, C, stride, T0, y, ss, gamma, beta, eps, s);
+    return conv0_k<half_t>(k, pcm, valid, L, B, w0, bias, C, stride, T0, y, ss, gamma, beta, eps, act, s);
+  return conv0_k<float>(k, pcm, valid, L, B, w0, bias, C, stride, T0, y, ss, gamma, beta, eps, act, s);
 }
 
 hipError_t launch_gn0_stats(const float* pcm, const int32_t* valid, int32_t L, int32_t B, int32_t k, int32_t stride,

@@ -69,16 +69,14 @@ __device__ inline int xcd_remap(int pid, int nb) {
 
 // Epilogue for 4 consecutive output columns nb..nb+3 of row m:
 // v = acc + bias; v = act(v); v += residual; store fp32 and/or operand type.
-template <typename T>
+template <typename T, int ACT>
 __device__ inline void epilogue4(const GemmArgs& a, const float* bias, int64_t rowoff, int nb, f4 v, bool vec) {
   if (vec) {
     if (bias) {
       const float4 bb = *(const float4*)(bias + nb);
       v.x += bb.x; v.y += bb.y; v.z += bb.z; v.w += bb.w;
     }
-    if (a.act == 1) {
-      v.x = gelu_erf(v.x); v.y = gelu_erf(v.y); v.z = gelu_erf(v.z); v.w = gelu_erf(v.w);
-    }
+    v.x = act_fn<ACT>(v.x); v.y = act_fn<ACT>(v.y); v.z = act_fn<ACT>(v.z); v.w = act_fn<ACT>(v.w);
     if (a.residual) {
       const float4 rr = *(const float4*)(a.residual + rowoff + nb);
       v.x += rr.x; v.y += rr.y; v.z += rr.z; v.w += rr.w;
@@ -99,13 +97,18 @@ __device__ inline void epilogue4(const GemmArgs& a, const float* bias, int64_t r
       if (n >= a.N) break;
       float x = v[r];
       if (bias) x += bias[n];
-      if (a.act == 1) x = gelu_erf(x);
+      x = act_fn<ACT>(x);
       if (a.residual) x += a.residual[rowoff + n];
       if (a.out_f32) a.out_f32[rowoff + n] = x;
       if (a.out_t) ((T*)a.out_t)[rowoff + n] = (T)x;
     }
   }
 }
+
+template <int N>
+struct ActTag {
+  static constexpr int value = N;
+};
 
 __device__ inline bool epilogue_vec_ok(const GemmArgs& a) {
   return ((a.ldc & 3) == 0) && ((a.N & 3) == 0) && ((a.c_group & 3) == 0) && ((a.bias_group & 3) == 0);
@@ -233,184 +236,27 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   const bool vec = epilogue_vec_ok(a);
   const float* bias = a.bias ? a.bias + (int64_t)group * a.bias_group : nullptr;
   const int64_t cg = (int64_t)group * a.c_group;
+  auto store_all = [&](auto act_tag) {
+    constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const int m = m0 + wm * TM * 16 + j * 16 + lr;
-    if (m >= a.M) continue;
-    const int64_t rowoff = cg + (int64_t)m * a.ldc;
+    for (int j = 0; j < TM; ++j) {
+      const int m = m0 + wm * TM * 16 + j * 16 + lr;
+      if (m >= a.M) continue;
+      const int64_t rowoff = cg + (int64_t)m * a.ldc;
 #pragma unroll
-    for (int i = 0; i < TN; ++i) {
-      const int nb = n0 + wn * TN * 16 + i * 16 + lg * 4;
-      if (nb < a.N) epilogue4<T>(a, bias, rowoff, nb, acc[i][j], vec);
-    }
-  }
-}
-
-// ----------------------------------------------------------------------------
-// fp16 kernel on v_mfma_f32_32x32x16_f16 with large wave tiles.
-// A wave owns (TN*32) x (TM*32) outputs; per 16-wide K slice it reads TN + TM
-// fragments from LDS and issues TN*TM MFMAs, so a 128x128 wave tile needs
-// half the LDS bytes per flop of the 64x64 / 16x16 layout above.  In the
-// 32x32 output block a lane holds activation row (lane % 32) and weight
-// columns 8q + 4*(lane / 32) + {0..3}, q = 0..3.
-// ----------------------------------------------------------------------------
-typedef float f16x __attribute__((ext_vector_type(16)));
-
-template <int BM, int BN, int WM, int WN, int ROLE>
-__global__ __launch_bounds__(256, 1) void gemm_f16_kernel(GemmArgs a) {
-  constexpr int TM = BM / WM / 32;
-  constexpr int TN = BN / WN / 32;
-  constexpr int BK = 64;                 // halves per 128-byte tile row
-  constexpr int NLA = BM * 8 / 256;
-  constexpr int NLB = BN * 8 / 256;
-  static_assert(WM * WN == 4 && TM >= 1 && TN >= 1, "4 waves");
-
-  __shared__ uint4 sA[2][BM * kPitch];
-  __shared__ uint4 sB[2][BN * kPitch];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int group = blockIdx.z;
-
-  const int tiles_m = (a.M + BM - 1) / BM;
-  const int tiles_n = (a.N + BN - 1) / BN;
-  const int pid = xcd_remap(blockIdx.x, gridDim.x);
-  constexpr int GM = 8;
-  const int width = GM * tiles_n;
-  const int first_m = (pid / width) * GM;
-  const int gsz = min(tiles_m - first_m, GM);
-  const int tm = first_m + (pid % width) % gsz;
-  const int tn = (pid % width) / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  const char* Abase = (const char*)a.A + (int64_t)group * a.a_group * 2;
-  const char* Bbase = (const char*)a.B + (int64_t)group * a.b_group * 2;
-
-  const char* arow[NLA];
-  bool aok[NLA];
-#pragma unroll
-  for (int i = 0; i < NLA; ++i) {
-    const int idx = tid + 256 * i;
-    const int m = m0 + (idx >> 3);
-    aok[i] = m < a.M;
-    const int mm = aok[i] ? m : 0;
-    const int seg = mm / a.seg_rows, t = mm - seg * a.seg_rows;
-    arow[i] = Abase + ((int64_t)seg * a.a_seg + (int64_t)t * a.lda) * 2 + (idx & 7) * 16;
-  }
-  const char* brow[NLB];
-  bool bok[NLB];
-#pragma unroll
-  for (int i = 0; i < NLB; ++i) {
-    const int idx = tid + 256 * i;
-    const int n = n0 + (idx >> 3);
-    bok[i] = n < a.N;
-    brow[i] = Bbase + ((int64_t)(bok[i] ? n : 0) * a.K) * 2 + (idx & 7) * 16;
-  }
-
-  uint4 ra[NLA], rb[NLB];
-  auto load = [&](int kt) {
-    const int kbase = kt * BK;
-#pragma unroll
-    for (int i = 0; i < NLA; ++i) {
-      const int idx = tid + 256 * i;
-      const bool ok = aok[i] && (kbase + (idx & 7) * 8 < a.K);
-      ra[i] = ok ? *(const uint4*)(arow[i] + (int64_t)kbase * 2) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < NLB; ++i) {
-      const int idx = tid + 256 * i;
-      const bool ok = bok[i] && (kbase + (idx & 7) * 8 < a.K);
-      rb[i] = ok ? *(const uint4*)(brow[i] + (int64_t)kbase * 2) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NLA; ++i) {
-      const int idx = tid + 256 * i;
-      sA[buf][(idx >> 3) * kPitch + (idx & 7)] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NLB; ++i) {
-      const int idx = tid + 256 * i;
-      sB[buf][(idx >> 3) * kPitch + (idx & 7)] = rb[i];
-    }
-  };
-
-  f16x acc[TN][TM];
-#pragma unroll
-  for (int i = 0; i < TN; ++i)
-#pragma unroll
-    for (int j = 0; j < TM; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  const int nk = (a.K + BK - 1) / BK;
-  load(0);
-  store(0);
-  __syncthreads();
-
-  const int l32 = lane & 31, lg = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint4 wv[TN], av[TM];
-#pragma unroll
-      for (int i = 0; i < TN; ++i) wv[i] = sB[cur][(wn * TN * 32 + i * 32 + l32) * kPitch + ks * 2 + lg];
-#pragma unroll
-      for (int j = 0; j < TM; ++j) av[j] = sA[cur][(wm * TM * 32 + j * 32 + l32) * kPitch + ks * 2 + lg];
-#pragma unroll
-      for (int i = 0; i < TN; ++i)
-#pragma unroll
-        for (int j = 0; j < TM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, wv[i]),
-                                                             __builtin_bit_cast(h8, av[j]), acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store(cur ^ 1);
-    __syncthreads();
-  }
-
-  const bool vec = epilogue_vec_ok(a);
-  const float* bias = a.bias ? a.bias + (int64_t)group * a.bias_group : nullptr;
-  const int64_t cg = (int64_t)group * a.c_group;
-#pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const int m = m0 + wm * TM * 32 + j * 32 + l32;
-    if (m >= a.M) continue;
-    const int64_t rowoff = cg + (int64_t)m * a.ldc;
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nb = n0 + wn * TN * 32 + i * 32 + 8 * q + 4 * lg;
-        if (nb < a.N) {
-          const f4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          epilogue4<half_t>(a, bias, rowoff, nb, v, vec);
-        }
+      for (int i = 0; i < TN; ++i) {
+        const int nb = n0 + wn * TN * 16 + i * 16 + lg * 4;
+        if (nb < a.N) epilogue4<T, ACT>(a, bias, rowoff, nb, acc[i][j], vec);
       }
     }
-  }
+  };
+  if (a.act == 1) store_all(ActTag<1>{});
+  else if (a.act == 2) store_all(ActTag<2>{});
+  else store_all(ActTag<0>{});
 }
 
-// ----------------------------------------------------------------------------
-// fp16 kernel with direct global->LDS loads (gfx950 global_load_lds_dwordx4)
-// and a STAGES-deep LDS ring.  Requires K % 64 == 0.
-//
-// Each wave-wide load instruction moves 1 KB: lane l's 16 bytes land at LDS
-// base + 16*l, i.e. 8 tile rows of 128 bytes.  Lane l therefore fetches row
-// r = 8*j + l/8 of its slice and the global chunk c = (l % 8) ^ ((r / 2) % 8),
-// so the row's chunks sit XOR-swizzled in LDS and the MFMA fragment reads
-// (16 lanes on 16 consecutive rows, same chunk) hit 16 distinct bank groups.
-// Rows beyond M or N are clamped to the last valid row (their outputs are
-// never stored), so every load is unconditional and in bounds.
-//
-// Pipeline: loads for K step kt + STAGES - 1 are issued right after the
-// barrier that publishes step kt, and step kt waits (vmcnt) only for its own
-// loads, so STAGES - 1 steps stay in flight during the MFMA work.
-// ----------------------------------------------------------------------------
+typedef float f16x __attribute__((ext_vector_type(16)));
+
 // One wave-wide direct global->LDS load: lane l's 16 bytes at gptr land at
 // LDS byte address lds + 16*l.  Written as inline asm so that the compiler's
 // wait-count pass does not treat every later LDS read as dependent on it (it
@@ -590,23 +436,29 @@ __global__ __launch_bounds__(256, 1) void gemm_dlds_kernel(GemmArgs a) {
   const bool vec = epilogue_vec_ok(a);
   const float* bias = a.bias ? a.bias + (int64_t)group * a.bias_group : nullptr;
   const int64_t cg = (int64_t)group * a.c_group;
+  auto store_all = [&](auto act_tag) {
+    constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const int m = m0 + wm * TM * 32 + j * 32 + l32;
-    if (m >= a.M) continue;
-    const int64_t rowoff = cg + (int64_t)m * a.ldc;
+    for (int j = 0; j < TM; ++j) {
+      const int m = m0 + wm * TM * 32 + j * 32 + l32;
+      if (m >= a.M) continue;
+      const int64_t rowoff = cg + (int64_t)m * a.ldc;
 #pragma unroll
-    for (int i = 0; i < TN; ++i) {
+      for (int i = 0; i < TN; ++i) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nb = n0 + wn * TN * 32 + i * 32 + 8 * q + 4 * lg;
-        if (nb < a.N) {
-          const f4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          epilogue4<half_t>(a, bias, rowoff, nb, v, vec);
+        for (int q = 0; q < 4; ++q) {
+          const int nb = n0 + wn * TN * 32 + i * 32 + 8 * q + 4 * lg;
+          if (nb < a.N) {
+            const f4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            epilogue4<half_t, ACT>(a, bias, rowoff, nb, v, vec);
+          }
         }
       }
     }
-  }
+  };
+  if (a.act == 1) store_all(ActTag<1>{});
+  else if (a.act == 2) store_all(ActTag<2>{});
+  else store_all(ActTag<0>{});
 }
 
 template <typename T, int BM, int BN, int WM, int WN, int ROLE>

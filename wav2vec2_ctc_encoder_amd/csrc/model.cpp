@@ -130,6 +130,7 @@ std::string check_config(const w2v2_config& c, int* frames_out) {
   if (c.blank_id < 0 || c.blank_id >= c.vocab) return bad("blank_id must be in [0, vocab)");
   if (!(c.eps > 0.f) || !std::isfinite(c.eps)) return bad("eps must be positive and finite");
   if (c.precision != W2V2_FP32 && c.precision != W2V2_FP16) return bad("unknown precision");
+  if (c.gelu_kind != W2V2_GELU_ERF && c.gelu_kind != W2V2_GELU_TANH) return bad("unknown gelu_kind");
   if (c.max_batch < 1 || c.max_batch > 4096) return bad("max_batch must be in [1, 4096]");
   if (c.window < 1) return bad("window must be >= 1");
   int64_t n = c.window;
@@ -202,6 +203,7 @@ struct w2v2_model {
   w2v2_config cfg{};
   int device = 0;
   DType dt = DType::F16;
+  int act = 1;                // GELU code of the kernels: 1 erf, 2 tanh
   int T[W2V2_MAX_CONV] = {};  // frames after conv i
   int Tf = 0;                 // frames per window
 
@@ -295,12 +297,12 @@ w2v2_status run_frontend(w2v2_model* m, const float* pcm, const int32_t* valid, 
     W2V2_LAUNCH(m, s, "conv0_gn_gelu",
                 launch_conv0(dt, pcm, valid, c.window, B, (const float*)m->conv[0].w, m->conv[0].bias, C0,
                              c.conv_kernel[0], c.conv_stride[0], m->T[0], m->bufA, m->gn_ss, nullptr, nullptr,
-                             c.eps, s));
+                             c.eps, m->act, s));
   } else {
     W2V2_LAUNCH(m, s, "conv0_ln_gelu",
                 launch_conv0(dt, pcm, valid, c.window, B, (const float*)m->conv[0].w, m->conv[0].bias, C0,
                              c.conv_kernel[0], c.conv_stride[0], m->T[0], m->bufA, nullptr, m->conv[0].gamma,
-                             m->conv[0].beta, c.eps, s));
+                             m->conv[0].beta, c.eps, m->act, s));
   }
   const void* cur = m->bufA;
   int tin = m->T[0], cin = C0;
@@ -319,14 +321,14 @@ w2v2_status run_frontend(w2v2_model* m, const float* pcm, const int32_t* valid, 
     g.bias = m->conv[i].bias;
     g.out_t = out;
     g.ldc = c.conv_dim[i];
-    g.act = (c.feat_norm == W2V2_NORM_GROUP) ? 1 : 0;
+    g.act = (c.feat_norm == W2V2_NORM_GROUP) ? m->act : 0;
     static const char* kConvName[W2V2_MAX_CONV] = {"conv0",      "conv1_gemm", "conv2_gemm", "conv3_gemm",
                                                     "conv4_gemm", "conv5_gemm", "conv6_gemm", "conv7_gemm"};
     W2V2_LAUNCH(m, s, kConvName[i], launch_gemm(dt, g, s));
     if (c.feat_norm == W2V2_NORM_LAYER) {
       W2V2_LAUNCH(m, s, "conv_ln_gelu",
                   launch_layernorm(dt, nullptr, out, (int64_t)B * m->T[i], c.conv_dim[i], m->conv[i].gamma,
-                                   m->conv[i].beta, c.eps, nullptr, out, 1, s));
+                                   m->conv[i].beta, c.eps, nullptr, out, m->act, s));
     }
     cur = out;
     tin = m->T[i];
@@ -397,7 +399,7 @@ w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, h
     g.groups = G;
     g.bias = m->pos_bias;
     g.bias_group = Cg;
-    g.act = 1;
+    g.act = m->act;
     g.residual = m->h;
     g.out_f32 = m->h;
     g.ldc = d;
@@ -423,7 +425,7 @@ w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, h
     else
       W2V2_LAUNCH(m, s, "layernorm",
                   launch_layernorm(dt, m->h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, m->h, m->x, 0, s));
-    W2V2_TRY(gemm_linear(m, s, "gemm_ffn1", kGemmFFN1, m->x, M, F, d, L.w1, L.b1, 1, nullptr, nullptr, m->ffn, F));
+    W2V2_TRY(gemm_linear(m, s, "gemm_ffn1", kGemmFFN1, m->x, M, F, d, L.w1, L.b1, m->act, nullptr, nullptr, m->ffn, F));
     W2V2_TRY(gemm_linear(m, s, "gemm_ffn2", kGemmFFN2, m->ffn, M, d, F, L.w2, L.b2, 0, m->h, m->h, nullptr, d));
     if (!stable)
       W2V2_LAUNCH(m, s, "layernorm",
@@ -520,6 +522,7 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
   m->cfg = c;
   m->device = device;
   m->dt = c.precision == W2V2_FP16 ? DType::F16 : DType::F32;
+  m->act = c.gelu_kind == W2V2_GELU_TANH ? 2 : 1;
   {
     int64_t n = c.window;
     for (int i = 0; i < c.n_conv; ++i) {

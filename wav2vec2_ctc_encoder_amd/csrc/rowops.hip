@@ -87,7 +87,9 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const XT* x, int64_t R, 
       o.z = (v[i].z - mean) * rstd * g.z + b.z;
       o.w = (v[i].w - mean) * rstd * g.w + b.w;
       if (act == 1) {
-        o.x = gelu_erf(o.x); o.y = gelu_erf(o.y); o.z = gelu_erf(o.z); o.w = gelu_erf(o.w);
+        o.x = act_fn<1>(o.x); o.y = act_fn<1>(o.y); o.z = act_fn<1>(o.z); o.w = act_fn<1>(o.w);
+      } else if (act == 2) {
+        o.x = act_fn<2>(o.x); o.y = act_fn<2>(o.y); o.z = act_fn<2>(o.z); o.w = act_fn<2>(o.w);
       }
       if (y32) *(float4*)(y32 + row * C + c) = o;
       if (yt) store4<T>(yt + row * C + c, o);

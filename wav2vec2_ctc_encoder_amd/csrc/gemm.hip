@@ -114,6 +114,82 @@ __device__ inline bool epilogue_vec_ok(const GemmArgs& a) {
   return ((a.ldc & 3) == 0) && ((a.N & 3) == 0) && ((a.c_group & 3) == 0) && ((a.bias_group & 3) == 0);
 }
 
+typedef float f16x __attribute__((ext_vector_type(16)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+
+// Whole 8-column chunks everywhere: the staged epilogue below stores 16 B of
+// fp16 (32 B of fp32) per lane.
+__device__ inline bool epilogue_staged_ok(const GemmArgs& a) {
+  const uintptr_t ptrs = (uintptr_t)a.out_t | (uintptr_t)a.out_f32 | (uintptr_t)a.residual | (uintptr_t)a.bias;
+  return ((a.ldc & 7) == 0) && ((a.N & 7) == 0) && ((a.c_group & 7) == 0) && ((a.bias_group & 7) == 0) &&
+         ((ptrs & 15) == 0);
+}
+
+// Epilogue of one wave's (TM*32) x (TN*32) block of 32x32 MFMA accumulators
+// (lane l holds, for block (i, j), rows m = j*32 + l%32 and the 4 columns
+// n = i*32 + 8q + 4*(l/32) + 0..3 in elements 4q..4q+3).  That layout makes
+// direct stores scatter 16-byte pieces over 32 rows per instruction, so each
+// 32-row slab goes through the wave's own LDS region instead: bias and the
+// activation are applied in registers, the slab is written row-major (row
+// pitch padded by 16 bytes to spread the rows over the banks) and read back
+// with LPR consecutive lanes covering one row, so the residual loads and the
+// output stores move whole contiguous rows.  LDS operations of one wave run in
+// order, so no barrier is needed between the write and the read-back.
+template <int TM, int TN, int ACT>
+__device__ inline void epilogue_staged(const GemmArgs& a, f16x (&acc)[TN][TM], float* stage, int m_base,
+                                       int n_base, int group) {
+  constexpr int W = TN * 32;    // columns of the wave block
+  constexpr int P = W + 4;      // padded row pitch (floats)
+  constexpr int LPR = W / 8;    // lanes per row in the read-back
+  constexpr int RPP = 64 / LPR; // rows per read-back pass
+  const int lane = threadIdx.x & 63, l32 = lane & 31, lg = lane >> 5;
+  const float* bias = a.bias ? a.bias + (int64_t)group * a.bias_group : nullptr;
+  const int64_t cg = (int64_t)group * a.c_group;
+  const int rrow = lane / LPR, rcol = (lane % LPR) * 8;
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = i * 32 + 8 * q + 4 * lg;
+        const int n = n_base + nl;
+        float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        if (bias && n < a.N) {
+          const float4 bb = *(const float4*)(bias + n);
+          v.x += bb.x; v.y += bb.y; v.z += bb.z; v.w += bb.w;
+        }
+        v.x = act_fn<ACT>(v.x); v.y = act_fn<ACT>(v.y); v.z = act_fn<ACT>(v.z); v.w = act_fn<ACT>(v.w);
+        *(float4*)(stage + l32 * P + nl) = v;
+      }
+    }
+#pragma unroll
+    for (int ps = 0; ps < 32 / RPP; ++ps) {
+      const int row = ps * RPP + rrow;
+      const int m = m_base + j * 32 + row, n = n_base + rcol;
+      float4 x0 = *(const float4*)(stage + row * P + rcol);
+      float4 x1 = *(const float4*)(stage + row * P + rcol + 4);
+      if (m < a.M && n < a.N) {
+        const int64_t off = cg + (int64_t)m * a.ldc + n;
+        if (a.residual) {
+          const float4 r0 = *(const float4*)(a.residual + off), r1 = *(const float4*)(a.residual + off + 4);
+          x0.x += r0.x; x0.y += r0.y; x0.z += r0.z; x0.w += r0.w;
+          x1.x += r1.x; x1.y += r1.y; x1.z += r1.z; x1.w += r1.w;
+        }
+        if (a.out_f32) {
+          *(float4*)(a.out_f32 + off) = x0;
+          *(float4*)(a.out_f32 + off + 4) = x1;
+        }
+        if (a.out_t) {
+          const h8v hv = {(half_t)x0.x, (half_t)x0.y, (half_t)x0.z, (half_t)x0.w,
+                          (half_t)x1.x, (half_t)x1.y, (half_t)x1.z, (half_t)x1.w};
+          *(h8v*)((half_t*)a.out_t + off) = hv;
+        }
+      }
+    }
+  }
+}
+
 template <typename T, int BM, int BN, int WM, int WN, int ROLE>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   constexpr int TM = BM / WM / 16;
@@ -255,8 +331,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   else store_all(ActTag<0>{});
 }
 
-typedef float f16x __attribute__((ext_vector_type(16)));
-
 // One wave-wide direct global->LDS load: lane l's 16 bytes at gptr land at
 // LDS byte address lds + 16*l.  Written as inline asm so that the compiler's
 // wait-count pass does not treat every later LDS read as dependent on it (it
@@ -303,8 +377,11 @@ __global__ __launch_bounds__(256, 1) void gemm_dlds_kernel(GemmArgs a) {
   static_assert(WM * WN == 4 && TM >= 1 && TN >= 1, "4 waves");
   static_assert(JA >= 1 && JB >= 1 && LPS * (STAGES - 2) <= 63 && STAGES <= 5, "tile / vmcnt range");
 
-  __shared__ uint4 sA[STAGES][BM * CPR];
-  __shared__ uint4 sB[STAGES][BN * CPR];
+  // one array for both operands so that the epilogue can reuse all of it
+  __shared__ uint4 smem[STAGES * (BM + BN) * CPR];
+  uint4 (*sA)[BM * CPR] = reinterpret_cast<uint4 (*)[BM * CPR]>(smem);
+  uint4 (*sB)[BN * CPR] = reinterpret_cast<uint4 (*)[BN * CPR]>(smem + STAGES * BM * CPR);
+  static_assert(4 * 32 * (TN * 32 + 4) * 4 <= STAGES * (BM + BN) * CPR * 16, "epilogue staging fits");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -433,6 +510,16 @@ __global__ __launch_bounds__(256, 1) void gemm_dlds_kernel(GemmArgs a) {
     __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
   }
 
+  if (epilogue_staged_ok(a)) {
+    // every wave is done reading the stages before any overwrites them
+    __builtin_amdgcn_s_barrier();
+    float* stage = reinterpret_cast<float*>(smem) + wave * 32 * (TN * 32 + 4);
+    const int m_base = m0 + wm * TM * 32, n_base = n0 + wn * TN * 32;
+    if (a.act == 1) epilogue_staged<TM, TN, 1>(a, acc, stage, m_base, n_base, group);
+    else if (a.act == 2) epilogue_staged<TM, TN, 2>(a, acc, stage, m_base, n_base, group);
+    else epilogue_staged<TM, TN, 0>(a, acc, stage, m_base, n_base, group);
+    return;
+  }
   const bool vec = epilogue_vec_ok(a);
   const float* bias = a.bias ? a.bias + (int64_t)group * a.bias_group : nullptr;
   const int64_t cg = (int64_t)group * a.c_group;
@@ -482,10 +569,11 @@ hipError_t launch_shape(const GemmArgs& a, hipStream_t s) {
     // direct-to-LDS pipeline: whole 64-wide K steps, N wide enough to fill a tile
     if (a.K % 64 == 0 && a.N > 32) {
       const int64_t tiles128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.groups;
-      // 128x128 tiles win on the long conv GEMMs; below ~3 rounds of two
-      // tiles per CU, 128x64 tiles balance the CUs better (measured on the
-      // encoder shapes M = 6392, N = 768..3072).
-      if (a.N > 64 && tiles128 >= 1536) return launch_dlds<128, 128, 2, 128, ROLE>(a, s);
+      // 128x128 tiles read less per MFMA and win on the 512-wide conv GEMMs
+      // and wherever there are enough of them to keep two per CU busy for a
+      // few rounds; with fewer tiles (N = 768 at M ~ 6400, or the M ~ 3200
+      // shapes) 128x64 tiles balance the CUs better.  Measured on gfx950.
+      if (a.N > 64 && (a.N <= 512 || tiles128 >= 850)) return launch_dlds<128, 128, 2, 128, ROLE>(a, s);
       return launch_dlds<128, 64, 2, 128, ROLE>(a, s);
     }
   }

@@ -5,6 +5,6 @@ import this package.  See ``w2v2_oracle`` for the definitions and sources.
 """
 from .w2v2_oracle import (  # noqa: F401
     activation, conv1d, conv_out_len, ctc_collapse, ctc_head, encoder, feature_encoder, feed_forward,
-    fold_weight_norm, forward, frame_argmax, gelu, gelu_tanh, greedy_decode, group_norm_over_time,
+    fold_weight_norm, forward, forward_true_length, frame_argmax, gelu, gelu_tanh, greedy_decode, group_norm_over_time,
     layer_norm, num_frames, positional_conv, self_attention, softmax, valid_frames,
 )

@@ -320,6 +320,32 @@ def forward(cfg, W: dict, pcm: np.ndarray, valid: np.ndarray, dtype=np.float64):
     return ctc_head(W, h), valid_frames(cfg, valid)
 
 
+def forward_true_length(cfg, W: dict, pcm: np.ndarray, valid: np.ndarray, dtype=np.float64):
+    """Every row run as its own true-length clip: (logits [B, T, V], frames [B]).
+
+    Row b is the whole network applied to its first valid[b] samples alone,
+    as one clip of exactly that length (TensorRT README, "Wav2Vec2 CTC
+    layouts": the input is true-length PCM and no padded-batch attention mask
+    is introduced).  So the conv layers, the group norm over time, the
+    positional conv's zero padding and the attention of row b see only that
+    clip.  Results sit on the frame grid of the full window (T = frames of
+    pcm.shape[1] samples); frames at or after the row's own frame count are 0.
+    """
+    B, L = pcm.shape
+    T = num_frames(cfg, L)
+    out = np.zeros((B, T, cfg.vocab), dtype=np.dtype(dtype))
+    vf = np.zeros(B, np.int32)
+    for b in range(B):
+        v = int(min(max(int(valid[b]), 0), L))
+        n = num_frames(cfg, v)
+        vf[b] = n
+        if n == 0:
+            continue
+        logits, _ = forward(cfg, W, pcm[b:b + 1, :v], np.array([v], np.int32), dtype)
+        out[b, :n] = logits[0]
+    return out, vf
+
+
 # ----------------------------------------------------------------------------
 # greedy CTC decoding
 # ----------------------------------------------------------------------------

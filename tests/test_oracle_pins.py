@@ -494,6 +494,69 @@ def test_whole_network_matches_transformers_wav2vec2forctc(variant):
 
 
 # ----------------------------------------------------------------------------
+# true-length mode: every row is its own unpadded clip
+# ----------------------------------------------------------------------------
+@pytest.mark.slow
+@pytest.mark.parametrize("variant", ["group_postnorm", "layer_stable"])
+def test_true_length_rows_match_transformers_on_the_unpadded_clip(variant):
+    # rows of different true lengths, one of them the whole window
+    cfg = _tiny(batch=3, **_VARIANTS[variant])
+    W = synth.make_weights(cfg)
+    valid = np.array([cfg.window, 9321, 4410], np.int32)
+    pcm, _ = synth.make_pcm(cfg, valid=valid, pad_garbage=True)
+    ours, vf = oracle.forward_true_length(cfg, W, pcm, valid)
+    T = oracle.num_frames(cfg, cfg.window)
+    assert ours.shape == (3, T, cfg.vocab)
+    for b in range(3):
+        n = oracle.num_frames(cfg, int(valid[b]))
+        assert vf[b] == n
+        ref = _hf_logits(cfg, W, pcm[b:b + 1, :valid[b]])[0]
+        assert ref.shape == (n, cfg.vocab)
+        assert np.abs(ours[b, :n] - ref).max() < 1e-10
+        assert not ours[b, n:].any()
+
+
+def test_true_length_full_rows_equal_the_padded_window():
+    cfg = _tiny(batch=2)
+    W = synth.make_weights(cfg)
+    pcm, valid = synth.make_pcm(cfg, valid=np.array([cfg.window, cfg.window], np.int32))
+    a, va = oracle.forward_true_length(cfg, W, pcm, valid)
+    b, vb = oracle.forward(cfg, W, pcm, valid)
+    assert np.array_equal(va, vb)
+    assert np.array_equal(a, b)
+
+
+def test_true_length_rows_are_independent_and_differ_from_padded_mode():
+    cfg = _tiny(batch=2)
+    W = synth.make_weights(cfg)
+    valid = np.array([7000, 12000], np.int32)
+    pcm, _ = synth.make_pcm(cfg, valid=valid)
+    a, _ = oracle.forward_true_length(cfg, W, pcm, valid)
+    pcm2 = pcm.copy()
+    pcm2[1] = synth.make_pcm(cfg, seed=999, valid=valid)[0][1]
+    valid2 = valid.copy()
+    valid2[1] = 15000
+    b, _ = oracle.forward_true_length(cfg, W, pcm2, valid2)
+    assert np.array_equal(a[0], b[0])
+    # the padded window (group norm over the zero tail, attention over every
+    # frame) is a different computation for a short row
+    p, _ = oracle.forward(cfg, W, pcm, valid)
+    n = oracle.num_frames(cfg, 7000)
+    assert np.abs(p[0, :n] - a[0, :n]).max() > 1e-4
+
+
+def test_true_length_short_rows():
+    cfg = _tiny(batch=3)
+    W = synth.make_weights(cfg)
+    valid = np.array([0, 399, 400], np.int32)
+    pcm, _ = synth.make_pcm(cfg, valid=valid)
+    out, vf = oracle.forward_true_length(cfg, W, pcm, valid)
+    assert vf.tolist() == [0, 0, 1]
+    assert not out[0].any() and not out[1].any()
+    assert not out[2, 1:].any() and np.abs(out[2, 0]).max() > 0
+
+
+# ----------------------------------------------------------------------------
 # mutation tests: plant a mistake in the oracle and show a pin catches it
 # ----------------------------------------------------------------------------
 def _tanh_gelu(x):

@@ -213,6 +213,31 @@ w2v2_status w2v2_forward(w2v2_model* model, const float* pcm, const int32_t* val
                          float* logits, int32_t* vframes, void* stream);
 
 /*
+ * Whole network with every row taken as its own true-length clip ([TRT]
+ * "Wav2Vec2 CTC layouts": true-length PCM input, no padded-batch attention
+ * mask): row b is computed exactly as a single clip of its first valid[b]
+ * samples, so its conv layers, the group norm over time of conv 0, the
+ * positional conv's zero padding and the attention cover only that clip's
+ * frames.  The rows are packed inside the library, so the work scales with
+ * the valid audio rather than with batch x window.
+ *   pcm        dev fp32 [batch, window]; only the first valid[b] samples of
+ *              row b are read.
+ *   valid_host HOST int32 [batch]: valid samples per row, 0 <= valid[b] <=
+ *              window.  Read during the call (launch sizes depend on it); the
+ *              caller may reuse the array as soon as the call returns.
+ *   batch      1 <= batch <= max_batch.
+ *   logits     dev fp32 [batch, T, vocab] (T = frames per window): frame t of
+ *              row b for t < w2v2_num_frames(valid[b]), 0 for later frames.
+ *   vframes    dev int32 [batch] or NULL: w2v2_num_frames(valid[b]).
+ * Asynchronous on `stream` like w2v2_forward (the lengths are staged to the
+ * device on that stream).  Calls that share a model must not overlap.
+ * Errors: W2V2_E_ARG (null model/pcm/valid_host/logits, batch out of range,
+ * a valid[b] outside [0, window]), W2V2_E_DEVICE (copy or launch failure).
+ */
+w2v2_status w2v2_forward_true_length(w2v2_model* model, const float* pcm, const int32_t* valid_host,
+                                     int32_t batch, float* logits, int32_t* vframes, void* stream);
+
+/*
  * Feature-encoder stage only (conv 0 .. conv n-1 with their norms and GELU):
  *   features dev fp32 [batch, T, C_last] (channels-last).
  * Same pcm / valid / batch rules as w2v2_forward.  Together with

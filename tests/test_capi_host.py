@@ -160,6 +160,7 @@ def test_null_arguments_rejected():
     h = ctypes.c_void_p()
     assert lib.w2v2_create(None, None, 0, 0, ctypes.byref(h)) == L.E_ARG
     assert lib.w2v2_forward(None, None, None, 1, None, None, None) == L.E_ARG
+    assert lib.w2v2_forward_true_length(None, None, None, 1, None, None, None) == L.E_ARG
     assert lib.w2v2_forward_frontend(None, None, None, 1, None, None) == L.E_ARG
     assert lib.w2v2_forward_encoder(None, None, 1, None, None) == L.E_ARG
     assert lib.w2v2_ctc_greedy(None, None, 1, 10, 32, 0, None, None, None) == L.E_ARG

@@ -1,0 +1,186 @@
+"""GPU parity of the true-length mode (every row its own unpadded clip)
+against the CPU oracle's forward_true_length.
+
+Gates as for the padded window: fp32 max |logits - oracle| <= 1e-3 over the
+whole [B, T, V] output (frames past a row's own frames must be exactly 0);
+fp16 Pearson >= 0.999 and per-frame argmax agreement >= 99.5% over the
+rows' own frames; CTC ids bit-exact given the same argmax.  Two exact
+properties pin the packing: a row computes to the same bits alone or inside
+any batch, and a full-window row computes to the same bits as in the padded
+mode.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _pearson(a, b):
+    a = a.astype(np.float64).ravel()
+    b = b.astype(np.float64).ravel()
+    a -= a.mean()
+    b -= b.mean()
+    return float((a @ b) / np.sqrt((a @ a) * (b @ b)))
+
+
+@functools.lru_cache(maxsize=None)
+def _weights(cfg):
+    return synth.make_weights(cfg)
+
+
+def _pcm(cfg, valid):
+    return synth.make_pcm(cfg, valid=np.asarray(valid, np.int32), pad_garbage=True)[0]
+
+
+def _gpu_true_length(cfg, pcm, valid, precision=None, max_batch=None):
+    import wav2vec2_ctc_encoder_amd as w2
+    W = _weights(cfg)
+    with w2.Model(cfg, W, max_batch=max_batch or pcm.shape[0], precision=precision) as m:
+        logits, vf = m.forward_true_length(torch.from_numpy(pcm).cuda(), np.asarray(valid, np.int32))
+        ids, lens = w2.ctc_greedy(logits, vf, blank_id=cfg.blank_id)
+        torch.cuda.synchronize()
+        return logits.cpu().numpy(), vf.cpu().numpy(), ids.cpu().numpy(), lens.cpu().numpy()
+
+
+def _check_ids(cfg, logits, vf, ids, lens):
+    a = oracle.frame_argmax(logits)
+    for b in range(logits.shape[0]):
+        want = oracle.ctc_collapse(a[b, :vf[b]], cfg.blank_id)
+        assert lens[b] == len(want), (b, lens[b], len(want))
+        assert np.array_equal(ids[b, :lens[b]], want), b
+
+
+def _check_tail_zero(logits, vf):
+    for b in range(logits.shape[0]):
+        assert not logits[b, vf[b]:].any(), b
+
+
+# rows: no frames, 399 / 400 samples (0 / 1 frame), fewer frames than the
+# positional kernel, middle lengths, the whole window
+_TINY = synth.TINY_1S_B1
+_TINY_VALID = [0, 399, 400, 2000, 5555, 9321, 13000, 16000]
+_TINY_VARIANTS = {
+    "group_postnorm": _TINY,
+    "layer_stable_bias": _TINY.replace(feat_norm="layer", conv_bias=True, stable_layer_norm=True),
+    "head32_odd_pos_kernel": _TINY.replace(hidden=128, heads=4, pos_kernel=15),
+}
+
+
+@pytest.mark.parametrize("variant", sorted(_TINY_VARIANTS))
+def test_tiny_fp32_true_length_matches_oracle(variant):
+    cfg = _TINY_VARIANTS[variant].replace(batch=len(_TINY_VALID))
+    _say(f"true-length tiny fp32 {variant}")
+    valid = np.array(_TINY_VALID, np.int32)
+    pcm = _pcm(cfg, valid)
+    ref, vf_ref = oracle.forward_true_length(cfg, _weights(cfg), pcm, valid)
+    logits, vf, ids, lens = _gpu_true_length(cfg, pcm, valid, precision="fp32")
+    assert np.array_equal(vf, vf_ref)
+    err = np.abs(logits.astype(np.float64) - ref).max()
+    _say(f"fp32 max-abs {err:.3e}")
+    assert err <= 1e-3, err
+    _check_tail_zero(logits, vf)
+    _check_ids(cfg, logits, vf, ids, lens)
+
+
+def test_tiny_fp16_true_length_gates():
+    cfg = _TINY.replace(batch=len(_TINY_VALID), precision="fp16")
+    _say("true-length tiny fp16")
+    valid = np.array(_TINY_VALID, np.int32)
+    pcm = _pcm(cfg, valid)
+    ref, vf_ref = oracle.forward_true_length(cfg, _weights(cfg), pcm, valid)
+    logits, vf, ids, lens = _gpu_true_length(cfg, pcm, valid, precision="fp16")
+    assert np.array_equal(vf, vf_ref)
+    sel_g = np.concatenate([logits[i, :vf[i]] for i in range(len(vf))])
+    sel_r = np.concatenate([ref[i, :vf[i]] for i in range(len(vf))])
+    r = _pearson(sel_g, sel_r)
+    agree = float(np.mean(np.argmax(sel_g, -1) == np.argmax(sel_r, -1)))
+    _say(f"fp16 pearson {r:.6f} agreement {agree:.5f} over {len(sel_g)} frames")
+    assert r >= 0.999 and agree >= 0.995
+    _check_tail_zero(logits, vf)
+    _check_ids(cfg, logits, vf, ids, lens)
+
+
+@pytest.mark.parametrize("name,rows", [("base_16s_b8", (0, 5)), ("large_16s_b4", (1, 2))])
+def test_full_workload_true_length_fp16_sampled_rows(name, rows):
+    cfg = synth.PRESETS[name]
+    if name == "large_16s_b4":
+        valid = np.array([cfg.window, 96000, 41000, 0], np.int32)  # the preset has full rows only
+    else:
+        valid = synth.make_valid(cfg)
+    _say(f"true-length {name} fp16, oracle rows {rows}, valid {valid.tolist()}")
+    pcm = _pcm(cfg, valid)
+    logits, vf, ids, lens = _gpu_true_length(cfg, pcm, valid)
+    _check_tail_zero(logits, vf)
+    _check_ids(cfg, logits, vf, ids, lens)
+    rows = list(rows)
+    sub = cfg.replace(batch=len(rows))
+    ref, vf_ref = oracle.forward_true_length(sub, _weights(cfg), pcm[rows], valid[rows])
+    assert np.array_equal(vf[rows], vf_ref)
+    sel_g = np.concatenate([logits[r, :vf[r]] for r in rows])
+    sel_r = np.concatenate([ref[i, :vf_ref[i]] for i in range(len(rows))])
+    r = _pearson(sel_g, sel_r)
+    agree = float(np.mean(np.argmax(sel_g, -1) == np.argmax(sel_r, -1)))
+    _say(f"fp16 pearson {r:.6f} agreement {agree:.5f} over {len(sel_g)} frames")
+    assert r >= 0.999 and agree >= 0.995
+
+
+def test_row_bits_do_not_depend_on_the_batch():
+    cfg = synth.BASE_16S_B8.replace(layers=2)
+    valid = synth.make_valid(synth.BASE_16S_B8)
+    pcm = _pcm(cfg, valid)
+    _say(f"true-length batch independence, valid {valid.tolist()}")
+    whole, vf, _, _ = _gpu_true_length(cfg, pcm, valid)
+    for b in (0, 3, 7):
+        alone, vfa, _, _ = _gpu_true_length(cfg, pcm[b:b + 1], valid[b:b + 1], max_batch=8)
+        assert vfa[0] == vf[b]
+        assert np.array_equal(alone[0], whole[b]), b
+    # a different order of the same rows
+    perm = np.array([5, 2, 7, 0, 1, 6, 3, 4])
+    shuf, _, _, _ = _gpu_true_length(cfg, pcm[perm], valid[perm])
+    assert np.array_equal(shuf, whole[perm])
+
+
+def test_full_rows_equal_padded_mode_bitwise():
+    import wav2vec2_ctc_encoder_amd as w2
+    cfg = synth.BASE_10S_B1.replace(batch=2, layers=2)
+    valid = np.array([cfg.window, cfg.window], np.int32)
+    pcm = _pcm(cfg, valid)
+    _say("true-length full rows vs padded mode")
+    tl, vf_tl, _, _ = _gpu_true_length(cfg, pcm, valid)
+    with w2.Model(cfg, _weights(cfg), max_batch=2) as m:
+        lg, vf = m.forward(torch.from_numpy(pcm).cuda(), torch.from_numpy(valid).cuda())
+        torch.cuda.synchronize()
+        lg, vf = lg.cpu().numpy(), vf.cpu().numpy()
+    assert np.array_equal(vf, vf_tl)
+    assert np.array_equal(tl, lg)
+
+
+def test_true_length_rejects_bad_lengths():
+    import wav2vec2_ctc_encoder_amd as w2
+    cfg = _TINY.replace(batch=2)
+    _say("true-length argument checks")
+    pcm = torch.zeros(2, cfg.window, device="cuda")
+    with w2.Model(cfg, _weights(cfg), max_batch=2) as m:
+        for bad in ([-1, 100], [100, cfg.window + 1]):
+            with pytest.raises(w2.W2V2Error):
+                m.forward_true_length(pcm, np.array(bad, np.int32))
+        with pytest.raises(ValueError):
+            m.forward_true_length(pcm, np.array([1, 2, 3], np.int32))
+        # a valid call afterwards still works
+        logits, vf = m.forward_true_length(pcm, np.array([16000, 0], np.int32))
+        torch.cuda.synchronize()
+        assert vf.cpu().tolist() == [49, 0]
+        assert not logits[1].any()

@@ -152,6 +152,29 @@ class Model:
                                            _stream(stream)), "w2v2_forward")
         return logits, vframes
 
+    def forward_true_length(self, pcm: torch.Tensor, valid, logits: torch.Tensor | None = None,
+                            vframes: torch.Tensor | None = None, stream=None):
+        """Every row as its own true-length clip of valid[b] samples.
+
+        ``valid`` is a host array (numpy or CPU tensor) of int32 sample counts;
+        the library reads it during the call.  Frames past a row's own frame
+        count come back as 0."""
+        B = pcm.shape[0]
+        _need(pcm, torch.float32, (B, self.window), "pcm")
+        vh = np.ascontiguousarray(np.asarray(valid.cpu() if isinstance(valid, torch.Tensor) else valid,
+                                             dtype=np.int32))
+        if vh.shape != (B,):
+            raise ValueError(f"valid: expected host int32 [{B}], got shape {vh.shape}")
+        if logits is None:
+            logits = torch.empty(B, self.frames_per_window, self.vocab, dtype=torch.float32, device=pcm.device)
+        if vframes is None:
+            vframes = torch.empty(B, dtype=torch.int32, device=pcm.device)
+        _need(logits, torch.float32, (B, self.frames_per_window, self.vocab), "logits")
+        _need(vframes, torch.int32, (B,), "vframes")
+        _lib.check(_lib.lib().w2v2_forward_true_length(self._h, _ptr(pcm), vh.ctypes.data, B, _ptr(logits),
+                                                       _ptr(vframes), _stream(stream)), "w2v2_forward_true_length")
+        return logits, vframes
+
     def forward_frontend(self, pcm: torch.Tensor, valid: torch.Tensor, features: torch.Tensor | None = None,
                          stream=None) -> torch.Tensor:
         B = pcm.shape[0]

@@ -18,6 +18,9 @@
 // keys {16b + 4g + r}; the V^T operand reads the same keys from LDS, so the
 // contraction covers every key once.  Tail keys (>= T) get score -inf and
 // zero K/V rows.
+//
+// True-length rows: with per-row frame counts and packed starts, row b's
+// queries and keys are its own frames only (workgroups past them exit).
 #include "common.h"
 
 namespace w2v2 {
@@ -42,8 +45,8 @@ struct AttnCfg {
 };
 
 template <typename T, int DH>
-__global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qkv, T* __restrict__ out, int Tn,
-                                                        int H, float c1) {
+__global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qkv, T* __restrict__ out, int Tpad,
+                                                        RowSpan rows, int H, float c1) {
   using C = AttnCfg<T, DH>;
   __shared__ uint4 sK[kKT * C::KPITCH];
   __shared__ uint4 sV[DH * C::VPITCH];
@@ -51,9 +54,12 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int b = blockIdx.z, h = blockIdx.y;
+  const int Tn = rows.len ? rows.len[b] : Tpad;                                  // frames of this row
+  const int64_t rs = rows.start ? (int64_t)rows.start[b] : (int64_t)b * Tpad;    // its first row
+  if (blockIdx.x * kQ >= Tn) return;
   const int dm = H * DH;
   const int64_t ld = 3 * (int64_t)dm;
-  const T* base = qkv + (int64_t)b * Tn * ld;
+  const T* base = qkv + rs * ld;
   const int q0 = blockIdx.x * kQ + wave * 16;
 
   // zero the padded d range of K once (only when DH < one MFMA chunk)
@@ -181,7 +187,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
   const float inv = 1.f / lsum;
   const int q = q0 + lr;
   if (q < Tn) {
-    T* orow = out + ((int64_t)b * Tn + q) * dm + h * DH;
+    T* orow = out + (rs + q) * dm + h * DH;
 #pragma unroll
     for (int db = 0; db < C::ND; ++db) {
       const int d0 = db * 16 + lg * 4;
@@ -197,199 +203,6 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
 }
 
 // ----------------------------------------------------------------------------
-// fp16 kernel for d_head = 64 / 128 on v_mfma_f32_32x32x16_f16.
-// A wave owns 32 queries; S^T = K Q^T is built from 32x32 blocks (a lane
-// holds query lane % 32 and 16 of the 32 keys of a block: 8j + 4*(lane/32) +
-// {0..3}), so the row max / sum need one cross-lane step (lane ^ 32).  For
-// the second product O^T = V^T P^T the MFMA k-slots of a 16-key slice carry
-// keys {16s + 4g + i, 16s + 8 + 4g + i} (g = lane / 32, i < 4), exactly the
-// probabilities the lane already holds; V^T is read for the same keys.
-// K and V^T tiles of 64 keys are double-buffered in LDS, the next tile is
-// prefetched into registers while the current one is used, and only the
-// last tile (keys >= T) pays for masking.
-// ----------------------------------------------------------------------------
-typedef float f16x __attribute__((ext_vector_type(16)));
-
-template <int DH, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_f16_kernel(const half_t* __restrict__ qkv, half_t* __restrict__ out,
-                                                          int Tn, int H, float c1) {
-  constexpr int KT = 64;                     // keys per tile
-  constexpr int KP = DH / 8 + 1;             // K row pitch (16-byte units)
-  constexpr int VP = KT + 4;                 // V^T row pitch (halves): 136 bytes
-  constexpr int NDS = DH / 16;               // d slices of the score product
-  constexpr int NDB = DH / 32;               // 32-row d blocks of the output
-  constexpr int NT = NW * 64;
-  constexpr int KCH = KT * DH / 8;           // 16-byte chunks of a K tile
-  constexpr int KPT = (KCH + NT - 1) / NT;   // per thread
-  constexpr int VGR = KT * DH / 16;          // 4 keys x 4 d groups of a V tile
-  constexpr int VPT = (VGR + NT - 1) / NT;
-
-  __shared__ uint4 sK[2][KT * KP];
-  __shared__ half_t sV[2][DH * VP];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, g = lane >> 5;
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int dm = H * DH;
-  const int64_t ld = 3 * (int64_t)dm;
-  const half_t* base = qkv + (int64_t)b * Tn * ld + h * DH;
-  const int qw = blockIdx.x * (NW * 32) + wave * 32;  // this wave's first query
-  const bool wave_live = qw < Tn;
-
-  // Q fragments (B operand: column = query, k = d slice)
-  uint4 qf[NDS];
-  {
-    const int q = min(qw + l32, Tn - 1);
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) qf[ds] = *(const uint4*)(base + (int64_t)q * ld + ds * 16 + g * 8);
-  }
-
-  uint4 rk[KPT];
-  uint2 rv[VPT][4];
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int idx = tid + NT * i;
-      if (idx < KCH) {
-        const int key = k0 + idx / (DH / 8), ch = idx % (DH / 8);
-        rk[i] = key < Tn ? *(const uint4*)(base + (int64_t)key * ld + dm + ch * 8) : make_uint4(0, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int idx = tid + NT * i;
-      if (idx < VGR) {
-        const int dg = idx % (DH / 4), kg = idx / (DH / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = k0 + kg * 4 + r;
-          rv[i][r] = key < Tn ? *(const uint2*)(base + (int64_t)key * ld + 2 * dm + dg * 4) : make_uint2(0, 0);
-        }
-      }
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int idx = tid + NT * i;
-      if (idx < KCH) sK[buf][(idx / (DH / 8)) * KP + idx % (DH / 8)] = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int idx = tid + NT * i;
-      if (idx < VGR) {
-        const int dg = idx % (DH / 4), kg = idx / (DH / 4);
-        // transpose 4 keys x 4 d: row d gets keys kg*4 .. kg*4+3 (8 bytes)
-#pragma unroll
-        for (int dd = 0; dd < 4; ++dd) {
-          const half_t* e0 = (const half_t*)&rv[i][0];
-          const half_t* e1 = (const half_t*)&rv[i][1];
-          const half_t* e2 = (const half_t*)&rv[i][2];
-          const half_t* e3 = (const half_t*)&rv[i][3];
-          h4 col = {e0[dd], e1[dd], e2[dd], e3[dd]};
-          *(h4*)&sV[buf][(dg * 4 + dd) * VP + kg * 4] = col;
-        }
-      }
-    }
-  };
-
-  f16x o[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
-  float mrun = -INFINITY, lsum = 0.f;
-
-  const int ntile = (Tn + KT - 1) / KT;
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  for (int t = 0; t < ntile; ++t) {
-    const int cur = t & 1;
-    const int k0 = t * KT;
-    if (t + 1 < ntile) fetch(k0 + KT);
-    if (wave_live) {
-      // S^T for two 32-key blocks
-      f16x sc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-          const uint4 kf = sK[cur][(kb * 32 + l32) * KP + ds * 2 + g];
-          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, kf), __builtin_bit_cast(h8, qf[ds]),
-                                                          sc[kb], 0, 0, 0);
-        }
-      }
-      if (k0 + KT > Tn) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (k0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3) >= Tn) sc[kb][e] = -INFINITY;
-      }
-      float mt = sc[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sc[kb][e]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mnew = fmaxf(mrun, mt);
-      const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * c1);
-      const float mc = mnew * c1;
-      mrun = mnew;
-      float ps = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sc[kb][e], c1, -mc));
-          sc[kb][e] = pv;
-          ps += pv;
-        }
-      lsum = lsum * alpha + ps;
-#pragma unroll
-      for (int i = 0; i < NDB; ++i) o[i] *= alpha;
-      // O^T += V^T P^T over four 16-key slices
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int kb = ks >> 1, j0 = (ks & 1) * 2;
-        const h8 pf = {(half_t)sc[kb][4 * j0], (half_t)sc[kb][4 * j0 + 1], (half_t)sc[kb][4 * j0 + 2],
-                       (half_t)sc[kb][4 * j0 + 3], (half_t)sc[kb][4 * j0 + 4], (half_t)sc[kb][4 * j0 + 5],
-                       (half_t)sc[kb][4 * j0 + 6], (half_t)sc[kb][4 * j0 + 7]};
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const half_t* vrow = &sV[cur][(db * 32 + l32) * VP + ks * 16 + 4 * g];
-          const h4 va = *(const h4*)vrow;
-          const h4 vb = *(const h4*)(vrow + 8);
-          const h8 vf = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[db], 0, 0, 0);
-        }
-      }
-    }
-    if (t + 1 < ntile) stash(cur ^ 1);
-    __syncthreads();
-  }
-
-  if (!wave_live) return;
-  lsum += __shfl_xor(lsum, 32, 64);
-  const float inv = 1.f / lsum;
-  const int q = qw + l32;
-  if (q < Tn) {
-    half_t* orow = out + ((int64_t)b * Tn + q) * dm + h * DH;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const h4 hv = {(half_t)(o[db][4 * j] * inv), (half_t)(o[db][4 * j + 1] * inv),
-                       (half_t)(o[db][4 * j + 2] * inv), (half_t)(o[db][4 * j + 3] * inv)};
-        *(h4*)(orow + db * 32 + 8 * j + 4 * g) = hv;
-      }
-  }
-}
-
-// ----------------------------------------------------------------------------
 // fp16 kernel on v_mfma_f32_16x16x32_f16 with 16 queries per wave (small
 // register footprint, so several waves per SIMD hide the latency of the
 // dependent score -> softmax -> PV chain).  Same S^T / P^T layout as the
@@ -400,7 +213,7 @@ __global__ __launch_bounds__(NW * 64) void attn_f16_kernel(const half_t* __restr
 // ----------------------------------------------------------------------------
 template <int DH, int NW>
 __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restrict__ qkv, half_t* __restrict__ out,
-                                                        int Tn, int H, float c1) {
+                                                        int Tpad, RowSpan rows, int H, float c1) {
   constexpr int KT = 64;
   constexpr int KP = DH / 8 + 1;             // K row pitch (16-byte units)
   constexpr int VP = KT + 4;                 // V^T row pitch (halves)
@@ -418,9 +231,12 @@ __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restric
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int b = blockIdx.z, h = blockIdx.y;
+  const int Tn = rows.len ? rows.len[b] : Tpad;                                  // frames of this row
+  const int64_t rs = rows.start ? (int64_t)rows.start[b] : (int64_t)b * Tpad;    // its first row
+  if (blockIdx.x * (NW * 16) >= Tn) return;
   const int dm = H * DH;
   const int64_t ld = 3 * (int64_t)dm;
-  const half_t* base = qkv + (int64_t)b * Tn * ld + h * DH;
+  const half_t* base = qkv + rs * ld + h * DH;
   const int qw = blockIdx.x * (NW * 16) + wave * 16;
   const bool wave_live = qw < Tn;
 
@@ -560,7 +376,7 @@ __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restric
   const float inv = 1.f / lsum;
   const int q = qw + lr;
   if (q < Tn) {
-    half_t* orow = out + ((int64_t)b * Tn + q) * dm + h * DH;
+    half_t* orow = out + (rs + q) * dm + h * DH;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const h4 hv = {(half_t)(o[db][0] * inv), (half_t)(o[db][1] * inv), (half_t)(o[db][2] * inv),
@@ -571,36 +387,28 @@ __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restric
 }
 
 template <int DH, int NW>
-hipError_t launch_a16(const void* qkv, void* out, int B, int Tn, int H, hipStream_t s) {
+hipError_t launch_a16(const void* qkv, void* out, int B, int Tn, RowSpan rows, int H, hipStream_t s) {
   const float c1 = 1.4426950408889634f / sqrtf((float)DH);
   hipLaunchKernelGGL((attn16_kernel<DH, NW>), dim3((Tn + NW * 16 - 1) / (NW * 16), H, B), dim3(NW * 64), 0, s,
-                     (const half_t*)qkv, (half_t*)out, Tn, H, c1);
-  return hipGetLastError();
-}
-
-template <int DH, int NW>
-hipError_t launch_f16(const void* qkv, void* out, int B, int Tn, int H, hipStream_t s) {
-  const float c1 = 1.4426950408889634f / sqrtf((float)DH);
-  hipLaunchKernelGGL((attn_f16_kernel<DH, NW>), dim3((Tn + NW * 32 - 1) / (NW * 32), H, B), dim3(NW * 64), 0, s,
-                     (const half_t*)qkv, (half_t*)out, Tn, H, c1);
+                     (const half_t*)qkv, (half_t*)out, Tn, rows, H, c1);
   return hipGetLastError();
 }
 
 template <typename T, int DH>
-hipError_t launch_t(const void* qkv, void* out, int B, int Tn, int H, hipStream_t s) {
+hipError_t launch_t(const void* qkv, void* out, int B, int Tn, RowSpan rows, int H, hipStream_t s) {
   const float c1 = 1.4426950408889634f / sqrtf((float)DH);  // log2(e) / sqrt(dh)
   hipLaunchKernelGGL((attention_kernel<T, DH>), dim3((Tn + kQ - 1) / kQ, H, B), dim3(256), 0, s,
-                     (const T*)qkv, (T*)out, Tn, H, c1);
+                     (const T*)qkv, (T*)out, Tn, rows, H, c1);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_dh(const void* qkv, void* out, int B, int Tn, int H, int dh, hipStream_t s) {
+hipError_t launch_dh(const void* qkv, void* out, int B, int Tn, RowSpan rows, int H, int dh, hipStream_t s) {
   switch (dh) {
-    case 16: return launch_t<T, 16>(qkv, out, B, Tn, H, s);
-    case 32: return launch_t<T, 32>(qkv, out, B, Tn, H, s);
-    case 64: return launch_t<T, 64>(qkv, out, B, Tn, H, s);
-    case 128: return launch_t<T, 128>(qkv, out, B, Tn, H, s);
+    case 16: return launch_t<T, 16>(qkv, out, B, Tn, rows, H, s);
+    case 32: return launch_t<T, 32>(qkv, out, B, Tn, rows, H, s);
+    case 64: return launch_t<T, 64>(qkv, out, B, Tn, rows, H, s);
+    case 128: return launch_t<T, 128>(qkv, out, B, Tn, rows, H, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -609,14 +417,15 @@ hipError_t launch_dh(const void* qkv, void* out, int B, int Tn, int H, int dh, h
 
 bool attention_supported(int dh) { return dh == 16 || dh == 32 || dh == 64 || dh == 128; }
 
-hipError_t launch_attention(DType t, const void* qkv, void* out, int32_t B, int32_t T, int32_t H, int32_t dh,
-                            hipStream_t s) {
+hipError_t launch_attention(DType t, const void* qkv, void* out, int32_t B, int32_t T, RowSpan rows, int32_t H,
+                            int32_t dh, hipStream_t s) {
   if (B <= 0 || T <= 0) return hipSuccess;
   // fp16: 16 queries per wave, 8 waves share each K/V tile
-  if (t == DType::F16 && dh == 32) return launch_a16<32, 8>(qkv, out, B, T, H, s);
-  if (t == DType::F16 && dh == 64) return launch_a16<64, 8>(qkv, out, B, T, H, s);
-  if (t == DType::F16 && dh == 128) return launch_a16<128, 8>(qkv, out, B, T, H, s);
-  return t == DType::F16 ? launch_dh<half_t>(qkv, out, B, T, H, dh, s) : launch_dh<float>(qkv, out, B, T, H, dh, s);
+  if (t == DType::F16 && dh == 32) return launch_a16<32, 8>(qkv, out, B, T, rows, H, s);
+  if (t == DType::F16 && dh == 64) return launch_a16<64, 8>(qkv, out, B, T, rows, H, s);
+  if (t == DType::F16 && dh == 128) return launch_a16<128, 8>(qkv, out, B, T, rows, H, s);
+  return t == DType::F16 ? launch_dh<half_t>(qkv, out, B, T, rows, H, dh, s)
+                         : launch_dh<float>(qkv, out, B, T, rows, H, dh, s);
 }
 
 }  // namespace w2v2

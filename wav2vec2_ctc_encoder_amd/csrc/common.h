@@ -83,6 +83,12 @@ struct GemmArgs {
   const void* A = nullptr;
   int64_t lda = 0, a_seg = 0, a_group = 0;
   int32_t seg_rows = 1;
+  // Optional per-row tables (element offsets, M entries each): A row m starts
+  // at A + a_group * group + a_rows[m] instead of the segment rule
+  // seg * a_seg + t * lda; output row m starts at c_rows[m] instead of
+  // m * ldc (plus c_group * group in both cases).
+  const int64_t* a_rows = nullptr;
+  const int64_t* c_rows = nullptr;
   const void* B = nullptr;
   int64_t b_group = 0;
   int32_t M = 0, N = 0, K = 0, groups = 1;
@@ -108,21 +114,28 @@ hipError_t launch_gemm(DType t, const GemmArgs& a, hipStream_t s);
 //   group variant (gamma == null): y = GELU(conv * ss[b, c].x + ss[b, c].y),
 //     ss from gn0_finalize.
 //   layer variant (gamma != null): y = GELU(LN_c(conv + bias) * gamma + beta).
+// Per-row frames: rows.len (frames of row b, null: T0 for every row) and
+// rows.start (first packed output row of row b, null: b * T0).
+struct RowSpan {
+  const int32_t* len = nullptr;
+  const int32_t* start = nullptr;
+};
 hipError_t launch_conv0(DType t, const float* pcm, const int32_t* valid, int32_t L, int32_t B,
                         const float* w0, const float* bias, int32_t C, int32_t k, int32_t stride,
-                        int32_t T0, void* y, const float2* ss, const float* gamma, const float* beta,
-                        float eps, int32_t act, hipStream_t s);
+                        int32_t T0, RowSpan rows, void* y, const float2* ss, const float* gamma,
+                        const float* beta, float eps, int32_t act, hipStream_t s);
 // GroupNorm statistics of conv 0 from the PCM alone: per-chunk means and
 // co-moments of the k shifted sample sequences (fp64), then per (b, c)
 // scale = gamma * rstd and shift = beta - mean * scale.
 // Workspace: B * gn0_partial_doubles(k, T0) doubles (chunk partials, then the
 // per-row merged statistics behind them).
 int64_t gn0_partial_doubles(int32_t k, int32_t T0);  // per row
+// With rows_len set, row b's statistics cover its own rows_len[b] frames.
 hipError_t launch_gn0_stats(const float* pcm, const int32_t* valid, int32_t L, int32_t B, int32_t k, int32_t stride,
-                            int32_t T0, double* part, hipStream_t s);
-hipError_t launch_gn0_finalize(double* part, int32_t B, int32_t k, int32_t T0, const float* w0, const float* bias,
-                               int32_t C, const float* gamma, const float* beta, float eps, float2* ss,
-                               hipStream_t s);
+                            int32_t T0, const int32_t* rows_len, double* part, hipStream_t s);
+hipError_t launch_gn0_finalize(double* part, int32_t B, int32_t k, int32_t T0, const int32_t* rows_len,
+                               const float* w0, const float* bias, int32_t C, const float* gamma,
+                               const float* beta, float eps, float2* ss, hipStream_t s);
 
 // ----------------------------------------------------------------------------
 // row kernels
@@ -135,12 +148,28 @@ hipError_t launch_layernorm(DType t, const float* x_f32, const void* x_t, int64_
                             const float* gamma, const float* beta, float eps, float* y_f32,
                             void* y_t, int32_t act, hipStream_t s);
 // Positional-conv input: h fp32 [B, T, d] -> zg [G][B][T + K][d/G] (operand
-// type) with `pad` zero frames before the data and zeros after it.
-hipError_t launch_pos_pack(DType t, const float* h, int32_t B, int32_t T, int32_t d, int32_t G,
+// type) with `pad` zero frames before the data and zeros after it.  With
+// rows set, h holds packed rows (row b's frame t at rows.start[b] + t) and
+// frames t >= rows.len[b] of row b are zero in zg as well.
+hipError_t launch_pos_pack(DType t, const float* h, int32_t B, int32_t T, RowSpan rows, int32_t d, int32_t G,
                            int32_t Kp, int32_t pad, void* zg, hipStream_t s);
 // dtype conversions [n]
 hipError_t launch_cast_to_f32(DType t, const void* x, float* y, int64_t n, hipStream_t s);
 hipError_t launch_cast_from_f32(DType t, const float* x, void* y, int64_t n, hipStream_t s);
+// Packed-row offset tables: for every table and row b, entries
+// out[start[b] + t] = base[b] + t * mul for t < len[b].
+struct RowTable {
+  const int32_t* start = nullptr;
+  const int32_t* len = nullptr;
+  const int64_t* base = nullptr;
+  int64_t mul = 0;
+  int64_t* out = nullptr;
+};
+constexpr int kMaxRowTables = 10;
+hipError_t launch_row_tables(const RowTable* tabs, int32_t n, int32_t B, int32_t tmax, hipStream_t s);
+// y [B, T, V] fp32: frames t >= len[b] of row b set to 0.
+hipError_t launch_zero_tail_frames(float* y, int32_t B, int32_t T, int32_t V, const int32_t* len,
+                                   hipStream_t s);
 // frames per row from valid samples (conv length rule)
 hipError_t launch_valid_frames(const int32_t* valid, int32_t B, int32_t window, int32_t n_conv,
                                const int32_t* kernel, const int32_t* stride, int32_t* vframes,
@@ -149,9 +178,11 @@ hipError_t launch_valid_frames(const int32_t* valid, int32_t B, int32_t window, 
 // ----------------------------------------------------------------------------
 // attention: qkv [B*T, 3d] (q | k | v, head h at columns h*dh), out [B*T, d]
 // ----------------------------------------------------------------------------
+// With rows set, row b has its own rows.len[b] frames starting at packed row
+// rows.start[b] of qkv and out, and attends over those frames only.
 bool attention_supported(int dh);
-hipError_t launch_attention(DType t, const void* qkv, void* out, int32_t B, int32_t T, int32_t H,
-                            int32_t dh, hipStream_t s);
+hipError_t launch_attention(DType t, const void* qkv, void* out, int32_t B, int32_t T, RowSpan rows,
+                            int32_t H, int32_t dh, hipStream_t s);
 
 // ----------------------------------------------------------------------------
 // CTC

@@ -22,6 +22,10 @@
 // accurate even when a filter cancels most of the input's energy.
 // Layer-norm variant: the per-frame LayerNorm over channels and the GELU are
 // done in registers with wave reductions before the single store.
+//
+// True-length rows: every kernel here can take a per-row frame count; conv 0
+// then writes row b's frames to consecutive packed rows from its own start,
+// and the statistics cover only that row's frames.
 #include "common.h"
 
 namespace w2v2 {
@@ -64,14 +68,18 @@ template <typename T, int KT>
 __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pcm, const int32_t* __restrict__ valid,
                                                      int L, const float* __restrict__ w0,
                                                      const float* __restrict__ bias, int C, int k, int stride,
-                                                     int T0, T* __restrict__ y, const float2* __restrict__ ss,
+                                                     int T0, RowSpan rows, T* __restrict__ y,
+                                                     const float2* __restrict__ ss,
                                                      const float* __restrict__ gamma,
                                                      const float* __restrict__ beta, float eps, int act) {
   extern __shared__ float smem[];
   const int b = blockIdx.y;
   const int chunk = blockIdx.x;
   const int t0 = chunk * kChunk;
-  const int nf = min(kChunk, T0 - t0);
+  const int Tb = rows.len ? rows.len[b] : T0;             // frames of this row
+  const int nf = min(kChunk, Tb - t0);
+  if (nf <= 0) return;
+  const int64_t ybase = rows.start ? (int64_t)rows.start[b] : (int64_t)b * T0;  // its first output row
   const int nsamp = (nf - 1) * stride + KT;
   float* xs = smem;                                  // [nsamp]
 
@@ -135,7 +143,7 @@ __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pc
         const float rstd = rsqrtf(wave_sum(q) * invC + eps);
 #pragma unroll
         for (int c = 0; c < kLanesC; ++c) v[c] = act_fn<ACT>((v[c] - mean) * rstd * g[c] + be[c]);
-        if (active) store8<T>(y + ((int64_t)b * T0 + t0 + f) * C + c0, v);
+        if (active) store8<T>(y + (ybase + t0 + f) * C + c0, v);
       }
     };
     if (act == 2) frames(ActTag<2>{});
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pc
       conv(f, v);
 #pragma unroll
       for (int c = 0; c < kLanesC; ++c) v[c] = act_fn<ACT>(fmaf(v[c], sc[c], sh[c]));
-      if (active) store8<T>(y + ((int64_t)b * T0 + t0 + f) * C + c0, v);
+      if (active) store8<T>(y + (ybase + t0 + f) * C + c0, v);
     }
   };
   if (act == 2) frames(ActTag<2>{});
@@ -172,13 +180,16 @@ __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pc
 // are added in a fixed order, so the result is deterministic.
 __global__ __launch_bounds__(256) void gn0_stats_kernel(const float* __restrict__ pcm,
                                                          const int32_t* __restrict__ valid, int L, int k,
-                                                         int stride, int T0, double* __restrict__ part) {
+                                                         int stride, int T0, const int32_t* __restrict__ rows_len,
+                                                         double* __restrict__ part) {
   extern __shared__ float xs[];  // [(kStatChunk - 1) * stride + k]
   __shared__ double red[256];
   __shared__ double mu[16];
   const int b = blockIdx.y, chunk = blockIdx.x;
   const int t0 = chunk * kStatChunk;
-  const int nf = min(kStatChunk, T0 - t0);
+  const int Tb = rows_len ? rows_len[b] : T0;  // frames of this row
+  const int nf = min(kStatChunk, Tb - t0);
+  if (nf <= 0) return;  // past the row's frames: the merge stops before this chunk
   const int nsamp = (nf - 1) * stride + k;
   int vl = valid[b];
   vl = vl < 0 ? 0 : (vl > L ? L : vl);
@@ -241,10 +252,13 @@ __global__ __launch_bounds__(256) void gn0_stats_kernel(const float* __restrict_
 // copies agree); threads e < k also carry mu_e.  Output per row:
 // [mu_0 .. mu_{k-1}, S as a full k x k matrix].
 __global__ __launch_bounds__(256) void gn0_merge_kernel(const double* __restrict__ part, int nchunk, int k, int T0,
+                                                         const int32_t* __restrict__ rows_len,
                                                          double* __restrict__ merged) {
   constexpr int kBatch = 16;
   __shared__ double stage[kBatch * 152];
   const int b = blockIdx.x, tid = threadIdx.x;
+  const int Tb = rows_len ? rows_len[b] : T0;
+  const int nuse = min(nchunk, (Tb + kStatChunk - 1) / kStatChunk);  // chunks holding frames of this row
   const int ns = k + k * (k + 1) / 2;
   const int npair = k * (k + 1) / 2;
   int pi = 0, pj = 0;
@@ -258,14 +272,14 @@ __global__ __launch_bounds__(256) void gn0_merge_kernel(const double* __restrict
   }
   double mi = 0.0, mj = 0.0, me = 0.0, S = 0.0, n = 0.0;
   const double* src = part + (int64_t)b * nchunk * ns;
-  for (int c0 = 0; c0 < nchunk; c0 += kBatch) {
-    const int nb = min(kBatch, nchunk - c0);
+  for (int c0 = 0; c0 < nuse; c0 += kBatch) {
+    const int nb = min(kBatch, nuse - c0);
     __syncthreads();
     for (int i = tid; i < nb * ns; i += 256) stage[i] = src[(int64_t)c0 * ns + i];
     __syncthreads();
     for (int c = 0; c < nb; ++c) {
       const double* pc = stage + c * ns;
-      const double m = (double)min(kStatChunk, T0 - (c0 + c) * kStatChunk);
+      const double m = (double)min(kStatChunk, Tb - (c0 + c) * kStatChunk);
       const double nn = n + m;
       const double f = m / nn;
       if (tid < npair) {
@@ -289,6 +303,7 @@ __global__ __launch_bounds__(256) void gn0_merge_kernel(const double* __restrict
 // Per (row, channel): mean = w.mu + bias, var = w^T S w / T0, then the affine
 // GroupNorm map folded into scale = gamma * rstd, shift = beta - mean * scale.
 __global__ __launch_bounds__(256) void gn0_finalize_kernel(const double* __restrict__ merged, int k, int T0,
+                                                            const int32_t* __restrict__ rows_len,
                                                             const float* __restrict__ w0,
                                                             const float* __restrict__ bias, int C,
                                                             const float* __restrict__ gamma,
@@ -310,7 +325,8 @@ __global__ __launch_bounds__(256) void gn0_finalize_kernel(const double* __restr
     for (int j = 0; j < k; ++j) r += st[k + i * k + j] * (double)w[j];
     q += wi * r;
   }
-  const double var = fmax(q / (double)T0, 0.0);
+  const int Tb = rows_len ? rows_len[b] : T0;  // a row without frames never uses its scale and shift
+  const double var = fmax(q / (double)max(Tb, 1), 0.0);
   const float rstd = (float)(1.0 / sqrt(var + (double)eps));
   const float scv = gamma[c] * rstd;
   ss[(int64_t)b * C + c] = make_float2(scv, beta[c] - (float)mean * scv);
@@ -334,22 +350,25 @@ __global__ void valid_frames_kernel(const int32_t* __restrict__ valid, int B, in
 
 template <typename T, int KT>
 hipError_t conv0_t(const float* pcm, const int32_t* valid, int32_t L, int32_t B, const float* w0,
-                   const float* bias, int32_t C, int32_t k, int32_t stride, int32_t T0, void* y, const float2* ss,
-                   const float* gamma, const float* beta, float eps, int32_t act, hipStream_t s) {
+                   const float* bias, int32_t C, int32_t k, int32_t stride, int32_t T0, RowSpan rows, void* y,
+                   const float2* ss, const float* gamma, const float* beta, float eps, int32_t act,
+                   hipStream_t s) {
   const int nchunk = (T0 + kChunk - 1) / kChunk;
   const int nsamp = (kChunk - 1) * stride + KT;
   const size_t lds = (size_t)((nsamp + 3) & ~3) * sizeof(float);
   hipLaunchKernelGGL((conv0_kernel<T, KT>), dim3(nchunk, B), dim3(256), lds, s, pcm, valid, L, w0, bias,
-                     C, k, stride, T0, (T*)y, ss, gamma, beta, eps, act);
+                     C, k, stride, T0, rows, (T*)y, ss, gamma, beta, eps, act);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t conv0_k(int k, const float* pcm, const int32_t* valid, int32_t L, int32_t B, const float* w0,
-                   const float* bias, int32_t C, int32_t stride, int32_t T0, void* y, const float2* ss,
-                   const float* gamma, const float* beta, float eps, int32_t act, hipStream_t s) {
-  if (k == 10) return conv0_t<T, 10>(pcm, valid, L, B, w0, bias, C, k, stride, T0, y, ss, gamma, beta, eps, act, s);
-  return conv0_t<T, 16>(pcm, valid, L, B, w0, bias, C, k, stride, T0, y, ss, gamma, beta, eps, act, s);
+                   const float* bias, int32_t C, int32_t stride, int32_t T0, RowSpan rows, void* y,
+                   const float2* ss, const float* gamma, const float* beta, float eps, int32_t act,
+                   hipStream_t s) {
+  if (k == 10)
+    return conv0_t<T, 10>(pcm, valid, L, B, w0, bias, C, k, stride, T0, rows, y, ss, gamma, beta, eps, act, s);
+  return conv0_t<T, 16>(pcm, valid, L, B, w0, bias, C, k, stride, T0, rows, y, ss, gamma, beta, eps, act, s);
 }
 
 }  // namespace
@@ -362,31 +381,32 @@ int64_t gn0_partial_doubles(int32_t k, int32_t T0) {
 
 hipError_t launch_conv0(DType t, const float* pcm, const int32_t* valid, int32_t L, int32_t B,
                         const float* w0, const float* bias, int32_t C, int32_t k, int32_t stride,
-                        int32_t T0, void* y, const float2* ss, const float* gamma, const float* beta,
-                        float eps, int32_t act, hipStream_t s) {
+                        int32_t T0, RowSpan rows, void* y, const float2* ss, const float* gamma,
+                        const float* beta, float eps, int32_t act, hipStream_t s) {
   if (t == DType::F16)
-    return conv0_k<half_t>(k, pcm, valid, L, B, w0, bias, C, stride, T0, y, ss, gamma, beta, eps, act, s);
-  return conv0_k<float>(k, pcm, valid, L, B, w0, bias, C, stride, T0, y, ss, gamma, beta, eps, act, s);
+    return conv0_k<half_t>(k, pcm, valid, L, B, w0, bias, C, stride, T0, rows, y, ss, gamma, beta, eps, act, s);
+  return conv0_k<float>(k, pcm, valid, L, B, w0, bias, C, stride, T0, rows, y, ss, gamma, beta, eps, act, s);
 }
 
 hipError_t launch_gn0_stats(const float* pcm, const int32_t* valid, int32_t L, int32_t B, int32_t k, int32_t stride,
-                            int32_t T0, double* part, hipStream_t s) {
+                            int32_t T0, const int32_t* rows_len, double* part, hipStream_t s) {
   const int nchunk = (T0 + kStatChunk - 1) / kStatChunk;
   const size_t lds = (size_t)((kStatChunk - 1) * stride + k) * sizeof(float);
-  hipLaunchKernelGGL(gn0_stats_kernel, dim3(nchunk, B), dim3(256), lds, s, pcm, valid, L, k, stride, T0, part);
+  hipLaunchKernelGGL(gn0_stats_kernel, dim3(nchunk, B), dim3(256), lds, s, pcm, valid, L, k, stride, T0, rows_len,
+                     part);
   return hipGetLastError();
 }
 
-hipError_t launch_gn0_finalize(double* part, int32_t B, int32_t k, int32_t T0, const float* w0, const float* bias,
-                               int32_t C, const float* gamma, const float* beta, float eps, float2* ss,
-                               hipStream_t s) {
+hipError_t launch_gn0_finalize(double* part, int32_t B, int32_t k, int32_t T0, const int32_t* rows_len,
+                               const float* w0, const float* bias, int32_t C, const float* gamma,
+                               const float* beta, float eps, float2* ss, hipStream_t s) {
   const int nchunk = (T0 + kStatChunk - 1) / kStatChunk;
   double* merged = part + (int64_t)B * nchunk * (k + k * (k + 1) / 2);
-  hipLaunchKernelGGL(gn0_merge_kernel, dim3(B), dim3(256), 0, s, part, nchunk, k, T0, merged);
+  hipLaunchKernelGGL(gn0_merge_kernel, dim3(B), dim3(256), 0, s, part, nchunk, k, T0, rows_len, merged);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gn0_finalize_kernel, dim3((C + 255) / 256, B), dim3(256), 0, s, merged, k, T0, w0, bias, C, gamma,
-                     beta, eps, ss);
+  hipLaunchKernelGGL(gn0_finalize_kernel, dim3((C + 255) / 256, B), dim3(256), 0, s, merged, k, T0, rows_len, w0,
+                     bias, C, gamma, beta, eps, ss);
   return hipGetLastError();
 }
 

@@ -110,6 +110,16 @@ struct ActTag {
   static constexpr int value = N;
 };
 
+// Element offset of A row m (before the group offset) and of output row m.
+__device__ inline int64_t a_row_offset(const GemmArgs& a, int m) {
+  if (a.a_rows) return a.a_rows[m];
+  const int seg = m / a.seg_rows, t = m - seg * a.seg_rows;
+  return (int64_t)seg * a.a_seg + (int64_t)t * a.lda;
+}
+__device__ inline int64_t c_row_offset(const GemmArgs& a, int m) {
+  return a.c_rows ? a.c_rows[m] : (int64_t)m * a.ldc;
+}
+
 __device__ inline bool epilogue_vec_ok(const GemmArgs& a) {
   return ((a.ldc & 3) == 0) && ((a.N & 3) == 0) && ((a.c_group & 3) == 0) && ((a.bias_group & 3) == 0);
 }
@@ -170,7 +180,7 @@ __device__ inline void epilogue_staged(const GemmArgs& a, f16x (&acc)[TN][TM], f
       float4 x0 = *(const float4*)(stage + row * P + rcol);
       float4 x1 = *(const float4*)(stage + row * P + rcol + 4);
       if (m < a.M && n < a.N) {
-        const int64_t off = cg + (int64_t)m * a.ldc + n;
+        const int64_t off = cg + c_row_offset(a, m) + n;
         if (a.residual) {
           const float4 r0 = *(const float4*)(a.residual + off), r1 = *(const float4*)(a.residual + off + 4);
           x0.x += r0.x; x0.y += r0.y; x0.z += r0.z; x0.w += r0.w;
@@ -234,8 +244,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     const int m = m0 + r;
     aok[i] = (idx < BM * 8) && (m < a.M);
     const int mm = aok[i] ? m : 0;
-    const int seg = mm / a.seg_rows, t = mm - seg * a.seg_rows;
-    arow[i] = Abase + ((int64_t)seg * a.a_seg + (int64_t)t * a.lda) * sizeof(T) + (idx & 7) * 16;
+    arow[i] = Abase + a_row_offset(a, mm) * sizeof(T) + (idx & 7) * 16;
   }
   const char* brow[NLB];
   bool bok[NLB];
@@ -318,7 +327,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     for (int j = 0; j < TM; ++j) {
       const int m = m0 + wm * TM * 16 + j * 16 + lr;
       if (m >= a.M) continue;
-      const int64_t rowoff = cg + (int64_t)m * a.ldc;
+      const int64_t rowoff = cg + c_row_offset(a, m);
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
         const int nb = n0 + wn * TN * 16 + i * 16 + lg * 4;
@@ -410,8 +419,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dlds_kernel(GemmArgs a) {
   for (int j = 0; j < JA; ++j) {
     const int r = (wave * JA + j) * RPI + lane / CPR;
     const int m = min(m0 + r, a.M - 1);
-    const int seg = m / a.seg_rows, t = m - seg * a.seg_rows;
-    asrc[j] = Abase + ((int64_t)seg * a.a_seg + (int64_t)t * a.lda) * 2 +
+    asrc[j] = Abase + a_row_offset(a, m) * 2 +
               ((pos ^ ((r / KEYDIV) & (CPR - 1))) << 4);
   }
   const char* bsrc[JB];
@@ -529,7 +537,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dlds_kernel(GemmArgs a) {
     for (int j = 0; j < TM; ++j) {
       const int m = m0 + wm * TM * 32 + j * 32 + l32;
       if (m >= a.M) continue;
-      const int64_t rowoff = cg + (int64_t)m * a.ldc;
+      const int64_t rowoff = cg + c_row_offset(a, m);
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
 #pragma unroll

@@ -17,6 +17,17 @@
 //   attention out        [B*T, d]        operand type
 //   FFN hidden           [B*T, ffn]      operand type
 //   pos-conv input       [G][B][T + K][d/G] operand type, zero padded
+//   true-length tables   per-level row lengths / packed starts (int32), the
+//                        table bases (int64) and the per-row offset tables
+//                        of the conv / positional-conv A operands and the
+//                        head's output rows (int64)
+//
+// True-length mode (w2v2_forward_true_length): every row is computed as its
+// own clip of valid[b] samples.  Rows are packed per level (row b's frames of
+// conv i at packed rows start_i[b] .. start_i[b] + len_i[b] - 1), so the conv
+// GEMMs, the encoder GEMMs and the row kernels run over the packed rows only;
+// the strided conv windows, the positional conv's padded input and the head's
+// [B, T, V] output rows are reached through the per-row offset tables.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -235,6 +246,10 @@ struct w2v2_model {
 
   // workspace regions
   void *bufA = nullptr, *bufB = nullptr;
+  int32_t* tl_i32 = nullptr;  // true-length: [2 * n_conv + 1][max_batch] lengths, starts, valid
+  int64_t* tl_base = nullptr; // [n_conv + 1][max_batch] table bases
+  int64_t* tl_rows = nullptr; // per-row offset tables
+  std::vector<int64_t> tl_host;  // host copy of the int32 + int64 part, uploaded per call
   double* gn_part = nullptr;
   float2* gn_ss = nullptr;
   float* h = nullptr;
@@ -282,27 +297,48 @@ size_t add_t(Arena& a, DType dt, const std::vector<float>& v) {
       return fail(W2V2_E_DEVICE, std::string(name) + ": " + hipGetErrorString(e_));  \
   } while (0)
 
+// int32 words of the true-length length/start/valid block (kept a multiple of 2
+// so that the int64 bases behind it stay aligned)
+int64_t tl_i32_words(const w2v2_config& c) { return (((int64_t)2 * c.n_conv + 1) * c.max_batch + 1) & ~int64_t(1); }
+// entries of the per-row tables: conv 1..n-1 A rows, positional-conv A rows, head output rows
+int64_t tl_rows_count(const w2v2_config& c, const int* T, int Tf) {
+  int64_t n = 2 * (int64_t)Tf;
+  for (int i = 1; i < c.n_conv; ++i) n += T[i];
+  return n * c.max_batch;
+}
+
+// True-length packing of one forward call (see the header); null: padded windows.
+struct Packing {
+  int64_t P[W2V2_MAX_CONV] = {};                 // packed rows per conv level
+  RowSpan lvl[W2V2_MAX_CONV];                    // per-row frames and starts (device)
+  const int64_t* a_rows[W2V2_MAX_CONV] = {};     // conv i >= 1: A row offsets
+  const int64_t* pos_rows = nullptr;             // positional-conv A row offsets
+  const int64_t* head_rows = nullptr;            // head output row offsets in [B, T, V]
+};
+
 // conv 0 .. n-1; returns the final conv output buffer in *feat
 w2v2_status run_frontend(w2v2_model* m, const float* pcm, const int32_t* valid, int B, hipStream_t s,
-                         const void** feat) {
+                         const void** feat, const Packing* pk = nullptr) {
   const w2v2_config& c = m->cfg;
   const DType dt = m->dt;
   const int C0 = c.conv_dim[0];
+  const RowSpan rows0 = pk ? pk->lvl[0] : RowSpan{};
   if (c.feat_norm == W2V2_NORM_GROUP) {
     W2V2_LAUNCH(m, s, "gn0_stats",
-                launch_gn0_stats(pcm, valid, c.window, B, c.conv_kernel[0], c.conv_stride[0], m->T[0], m->gn_part, s));
+                launch_gn0_stats(pcm, valid, c.window, B, c.conv_kernel[0], c.conv_stride[0], m->T[0], rows0.len,
+                                 m->gn_part, s));
     W2V2_LAUNCH(m, s, "gn0_finalize",
-                launch_gn0_finalize(m->gn_part, B, c.conv_kernel[0], m->T[0], (const float*)m->conv[0].w,
+                launch_gn0_finalize(m->gn_part, B, c.conv_kernel[0], m->T[0], rows0.len, (const float*)m->conv[0].w,
                                     m->conv[0].bias, C0, m->conv[0].gamma, m->conv[0].beta, c.eps, m->gn_ss, s));
     W2V2_LAUNCH(m, s, "conv0_gn_gelu",
                 launch_conv0(dt, pcm, valid, c.window, B, (const float*)m->conv[0].w, m->conv[0].bias, C0,
-                             c.conv_kernel[0], c.conv_stride[0], m->T[0], m->bufA, m->gn_ss, nullptr, nullptr,
-                             c.eps, m->act, s));
+                             c.conv_kernel[0], c.conv_stride[0], m->T[0], rows0, m->bufA, m->gn_ss, nullptr,
+                             nullptr, c.eps, m->act, s));
   } else {
     W2V2_LAUNCH(m, s, "conv0_ln_gelu",
                 launch_conv0(dt, pcm, valid, c.window, B, (const float*)m->conv[0].w, m->conv[0].bias, C0,
-                             c.conv_kernel[0], c.conv_stride[0], m->T[0], m->bufA, nullptr, m->conv[0].gamma,
-                             m->conv[0].beta, c.eps, m->act, s));
+                             c.conv_kernel[0], c.conv_stride[0], m->T[0], rows0, m->bufA, nullptr,
+                             m->conv[0].gamma, m->conv[0].beta, c.eps, m->act, s));
   }
   const void* cur = m->bufA;
   int tin = m->T[0], cin = C0;
@@ -314,8 +350,9 @@ w2v2_status run_frontend(w2v2_model* m, const float* pcm, const int32_t* valid, 
     g.lda = (int64_t)c.conv_stride[i] * cin;
     g.a_seg = (int64_t)tin * cin;
     g.seg_rows = m->T[i];
+    g.a_rows = pk ? pk->a_rows[i] : nullptr;
     g.B = m->conv[i].w;
-    g.M = B * m->T[i];
+    g.M = (int)(pk ? pk->P[i] : (int64_t)B * m->T[i]);
     g.N = c.conv_dim[i];
     g.K = c.conv_kernel[i] * cin;
     g.bias = m->conv[i].bias;
@@ -327,7 +364,7 @@ w2v2_status run_frontend(w2v2_model* m, const float* pcm, const int32_t* valid, 
     W2V2_LAUNCH(m, s, kConvName[i], launch_gemm(dt, g, s));
     if (c.feat_norm == W2V2_NORM_LAYER) {
       W2V2_LAUNCH(m, s, "conv_ln_gelu",
-                  launch_layernorm(dt, nullptr, out, (int64_t)B * m->T[i], c.conv_dim[i], m->conv[i].gamma,
+                  launch_layernorm(dt, nullptr, out, g.M, c.conv_dim[i], m->conv[i].gamma,
                                    m->conv[i].beta, c.eps, nullptr, out, m->act, s));
     }
     cur = out;
@@ -367,12 +404,14 @@ w2v2_status gemm_linear(w2v2_model* m, hipStream_t s, const char* name, int role
     if (st_ != W2V2_OK) return st_;     \
   } while (0)
 
-w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, hipStream_t s) {
+w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, hipStream_t s,
+                        const Packing* pk = nullptr) {
   const w2v2_config& c = m->cfg;
   const DType dt = m->dt;
   const int T = m->Tf, d = c.hidden, F = c.ffn, G = c.pos_groups, Cg = d / G, K = c.pos_kernel;
   const int cl = c.conv_dim[c.n_conv - 1];
-  const int M = B * T;
+  const int M = (int)(pk ? pk->P[c.n_conv - 1] : (int64_t)B * T);  // rows of the encoder
+  const RowSpan rows = pk ? pk->lvl[c.n_conv - 1] : RowSpan{};
   const float eps = c.eps;
 
   // feature projection: LN over channels, then Linear C -> d (fp32 residual stream)
@@ -382,7 +421,7 @@ w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, h
 
   // positional conv: h = z + GELU(posconv(z) + bias)
   const int pad = K / 2;
-  W2V2_LAUNCH(m, s, "pos_pack", launch_pos_pack(dt, m->h, B, T, d, G, K, pad, m->zg, s));
+  W2V2_LAUNCH(m, s, "pos_pack", launch_pos_pack(dt, m->h, B, T, rows, d, G, K, pad, m->zg, s));
   {
     GemmArgs g;
     g.role = kGemmPos;
@@ -390,6 +429,7 @@ w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, h
     g.lda = Cg;
     g.a_seg = (int64_t)(T + K) * Cg;
     g.seg_rows = T;
+    g.a_rows = pk ? pk->pos_rows : nullptr;
     g.a_group = (int64_t)B * (T + K) * Cg;
     g.B = m->pos_w;
     g.b_group = (int64_t)Cg * K * Cg;
@@ -417,7 +457,7 @@ w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, h
       W2V2_LAUNCH(m, s, "layernorm",
                   launch_layernorm(dt, m->h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, nullptr, m->x, 0, s));
     W2V2_TRY(gemm_linear(m, s, "gemm_qkv", kGemmQKV, m->x, M, 3 * d, d, L.wqkv, L.bqkv, 0, nullptr, nullptr, m->qkv, 3 * d));
-    W2V2_LAUNCH(m, s, "attention", launch_attention(dt, m->qkv, m->attn, B, T, c.heads, d / c.heads, s));
+    W2V2_LAUNCH(m, s, "attention", launch_attention(dt, m->qkv, m->attn, B, T, rows, c.heads, d / c.heads, s));
     W2V2_TRY(gemm_linear(m, s, "gemm_out_proj", kGemmOut, m->attn, M, d, d, L.wo, L.bo, 0, m->h, m->h, nullptr, d));
     if (stable)
       W2V2_LAUNCH(m, s, "layernorm",
@@ -434,8 +474,28 @@ w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, h
   if (stable)
     W2V2_LAUNCH(m, s, "layernorm",
                 launch_layernorm(dt, m->h, nullptr, M, d, m->enc_g, m->enc_b, eps, nullptr, m->x, 0, s));
-  W2V2_TRY(gemm_linear(m, s, "gemm_ctc_head", kGemmHead, m->x, M, c.vocab, d, m->head_w, m->head_b, 0, nullptr, logits,
-                       nullptr, c.vocab));
+  if (!pk) {
+    W2V2_TRY(gemm_linear(m, s, "gemm_ctc_head", kGemmHead, m->x, M, c.vocab, d, m->head_w, m->head_b, 0, nullptr,
+                         logits, nullptr, c.vocab));
+    return W2V2_OK;
+  }
+  // packed rows -> [B, T, V] through the output row table; frames past a
+  // row's own frames are zero
+  GemmArgs g;
+  g.role = kGemmHead;
+  g.A = m->x;
+  g.lda = d;
+  g.seg_rows = M > 0 ? M : 1;
+  g.B = m->head_w;
+  g.M = M;
+  g.N = c.vocab;
+  g.K = d;
+  g.bias = m->head_b;
+  g.out_f32 = logits;
+  g.ldc = c.vocab;
+  g.c_rows = pk->head_rows;
+  W2V2_LAUNCH(m, s, "gemm_ctc_head", launch_gemm(dt, g, s));
+  W2V2_LAUNCH(m, s, "zero_tail_frames", launch_zero_tail_frames(logits, B, T, c.vocab, rows.len, s));
   return W2V2_OK;
 }
 
@@ -696,6 +756,8 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
       (size_t)M * d * ds,                                 // attn
       (size_t)M * F * ds,                                 // ffn
       (size_t)G * Bm * (m->Tf + K) * Cg * ds,             // zg
+      (size_t)tl_i32_words(c) * 4 + (size_t)(c.n_conv + 1) * Bm * 8,   // true-length lengths/starts + bases
+      (size_t)tl_rows_count(c, m->T, m->Tf) * 8,          // true-length row tables
   };
   size_t total = 0;
   std::vector<size_t> offs;
@@ -718,6 +780,9 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
   m->x = wsb + offs[5];
   m->qkv = wsb + offs[6];
   m->attn = wsb + offs[7];
+  m->tl_i32 = (int32_t*)(wsb + offs[10]);
+  m->tl_base = (int64_t*)(wsb + offs[10] + (size_t)tl_i32_words(c) * 4);
+  m->tl_rows = (int64_t*)(wsb + offs[11]);
   m->ffn = wsb + offs[8];
   m->zg = wsb + offs[9];
   if (hipDeviceSynchronize() != hipSuccess) {
@@ -764,6 +829,95 @@ w2v2_status w2v2_forward(w2v2_model* m, const float* pcm, const int32_t* valid, 
     W2V2_LAUNCH(m, s, "valid_frames",
                 launch_valid_frames(valid, batch, m->cfg.window, m->cfg.n_conv, m->cfg.conv_kernel,
                                     m->cfg.conv_stride, vframes, s));
+  return W2V2_OK;
+}
+
+w2v2_status w2v2_forward_true_length(w2v2_model* m, const float* pcm, const int32_t* valid_host, int32_t batch,
+                                     float* logits, int32_t* vframes, void* stream) {
+  W2V2_TRY(check_forward_args(m, pcm, valid_host, batch, logits));
+  const w2v2_config& c = m->cfg;
+  const int n = c.n_conv, B = batch, Bm = c.max_batch;
+  for (int b = 0; b < B; ++b)
+    if (valid_host[b] < 0 || valid_host[b] > c.window)
+      return fail(W2V2_E_ARG, "valid[" + std::to_string(b) + "] must be in [0, window]");
+  DeviceGuard guard(m->device);
+  hipStream_t s = (hipStream_t)stream;
+
+  // host: frames and packed starts of every row at every conv level
+  const int64_t words = tl_i32_words(c);
+  std::vector<int64_t>& blob = m->tl_host;
+  blob.assign((size_t)(words / 2 + (int64_t)(n + 1) * Bm), 0);
+  int32_t* len = (int32_t*)blob.data();              // [n][Bm]
+  int32_t* start = len + (size_t)n * Bm;             // [n][Bm]
+  int32_t* vcopy = start + (size_t)n * Bm;           // [Bm]
+  int64_t* base = blob.data() + words / 2;           // [n + 1][Bm]
+  Packing pk;
+  for (int b = 0; b < B; ++b) {
+    vcopy[b] = valid_host[b];
+    int64_t f = valid_host[b];
+    for (int i = 0; i < n; ++i) {
+      f = conv_len(f, c.conv_kernel[i], c.conv_stride[i]);
+      len[(size_t)i * Bm + b] = (int32_t)f;
+    }
+  }
+  for (int i = 0; i < n; ++i) {
+    int64_t acc = 0;
+    for (int b = 0; b < B; ++b) {
+      start[(size_t)i * Bm + b] = (int32_t)acc;
+      acc += len[(size_t)i * Bm + b];
+    }
+    pk.P[i] = acc;
+  }
+  // table bases: conv i reads row b's input window at packed input row
+  // start_{i-1}[b] + t * stride_i; the positional conv reads row b's padded
+  // segment of T + K frames; the head writes row b's frame t at (b * T + t) * V
+  const int Tf = m->Tf, K = c.pos_kernel, Cg = c.hidden / c.pos_groups;
+  for (int i = 1; i < n; ++i)
+    for (int b = 0; b < B; ++b)
+      base[(size_t)(i - 1) * Bm + b] = (int64_t)start[(size_t)(i - 1) * Bm + b] * c.conv_dim[i - 1];
+  for (int b = 0; b < B; ++b) {
+    base[(size_t)(n - 1) * Bm + b] = (int64_t)b * (Tf + K) * Cg;
+    base[(size_t)n * Bm + b] = (int64_t)b * Tf * c.vocab;
+  }
+  // pageable source: the runtime stages it before returning, so the host
+  // block may be refilled by the next call
+  if (hipMemcpyAsync(m->tl_i32, blob.data(), blob.size() * sizeof(int64_t), hipMemcpyHostToDevice, s) != hipSuccess)
+    return fail(W2V2_E_DEVICE, "upload of the row lengths failed");
+
+  const int32_t* dlen = m->tl_i32;
+  const int32_t* dstart = m->tl_i32 + (size_t)n * Bm;
+  const int32_t* dvalid = m->tl_i32 + (size_t)2 * n * Bm;
+  for (int i = 0; i < n; ++i) {
+    pk.lvl[i].len = dlen + (size_t)i * Bm;
+    pk.lvl[i].start = dstart + (size_t)i * Bm;
+  }
+  RowTable tabs[kMaxRowTables];
+  int nt = 0, tmax = 1;
+  int64_t off = 0;
+  for (int i = 1; i < n; ++i) {
+    tabs[nt] = RowTable{pk.lvl[i].start, pk.lvl[i].len, m->tl_base + (size_t)(i - 1) * Bm,
+                        (int64_t)c.conv_stride[i] * c.conv_dim[i - 1], m->tl_rows + off};
+    pk.a_rows[i] = m->tl_rows + off;
+    off += (int64_t)Bm * m->T[i];
+    tmax = std::max(tmax, m->T[i]);
+    ++nt;
+  }
+  tabs[nt++] = RowTable{pk.lvl[n - 1].start, pk.lvl[n - 1].len, m->tl_base + (size_t)(n - 1) * Bm, Cg,
+                        m->tl_rows + off};
+  pk.pos_rows = m->tl_rows + off;
+  off += (int64_t)Bm * Tf;
+  tabs[nt++] = RowTable{pk.lvl[n - 1].start, pk.lvl[n - 1].len, m->tl_base + (size_t)n * Bm, c.vocab,
+                        m->tl_rows + off};
+  pk.head_rows = m->tl_rows + off;
+  tmax = std::max(tmax, Tf);
+  W2V2_LAUNCH(m, s, "row_tables", launch_row_tables(tabs, nt, B, tmax, s));
+
+  const void* feat = nullptr;
+  W2V2_TRY(run_frontend(m, pcm, dvalid, B, s, &feat, &pk));
+  W2V2_TRY(run_encoder(m, feat, B, logits, s, &pk));
+  if (vframes)
+    W2V2_LAUNCH(m, s, "valid_frames",
+                launch_valid_frames(dvalid, B, c.window, c.n_conv, c.conv_kernel, c.conv_stride, vframes, s));
   return W2V2_OK;
 }
 

@@ -112,8 +112,9 @@ hipError_t ln_dispatch(const XT* x, int64_t R, int C, const float* g, const floa
 
 // zg[g][b][p][i] = h[b, p - pad, g*Cg + i] for 0 <= p - pad < T, else 0.
 template <typename T>
-__global__ __launch_bounds__(256) void pos_pack_kernel(const float* __restrict__ h, int B, int Tn, int d, int G,
-                                                       int Tp, int pad, T* __restrict__ zg, int64_t nvec) {
+__global__ __launch_bounds__(256) void pos_pack_kernel(const float* __restrict__ h, int B, int Tn, RowSpan rows,
+                                                       int d, int G, int Tp, int pad, T* __restrict__ zg,
+                                                       int64_t nvec) {
   const int Cg = d / G;
   const int cv = Cg / 4;
   for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec;
@@ -125,9 +126,32 @@ __global__ __launch_bounds__(256) void pos_pack_kernel(const float* __restrict__
     const int b = (int)(r % B);
     const int g = (int)(r / B);
     const int t = p - pad;
+    const int Tb = rows.len ? rows.len[b] : Tn;
+    const int64_t hrow = rows.start ? (int64_t)rows.start[b] : (int64_t)b * Tn;
     float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t >= 0 && t < Tn) val = *(const float4*)(h + ((int64_t)b * Tn + t) * d + g * Cg + 4 * i4);
+    if (t >= 0 && t < Tb) val = *(const float4*)(h + (hrow + t) * d + g * Cg + 4 * i4);
     store4<T>(zg + v * 4, val);
+  }
+}
+
+// One thread per (table, row, frame): out[start[b] + t] = base[b] + t * mul.
+struct RowTables {
+  RowTable t[kMaxRowTables];
+};
+__global__ __launch_bounds__(256) void row_tables_kernel(RowTables rt) {
+  const RowTable& tb = rt.t[blockIdx.z];
+  const int b = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t < tb.len[b]) tb.out[(int64_t)tb.start[b] + t] = tb.base[b] + (int64_t)t * tb.mul;
+}
+
+// y [B, T, V]: zero every element of frames t >= len[b].
+__global__ __launch_bounds__(256) void zero_tail_kernel(float* __restrict__ y, int B, int T, int V,
+                                                        const int32_t* __restrict__ len, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t f = i / V;
+    const int t = (int)(f % T), b = (int)(f / T);
+    if (t >= len[b]) y[i] = 0.f;
   }
 }
 
@@ -161,16 +185,30 @@ hipError_t launch_layernorm(DType t, const float* x_f32, const void* x_t, int64_
   return ln_dispatch<float, float>((const float*)x_t, R, C, gamma, beta, eps, y_f32, (float*)y_t, act, s);
 }
 
-hipError_t launch_pos_pack(DType t, const float* h, int32_t B, int32_t T, int32_t d, int32_t G, int32_t Kp,
-                           int32_t pad, void* zg, hipStream_t s) {
+hipError_t launch_pos_pack(DType t, const float* h, int32_t B, int32_t T, RowSpan rows, int32_t d, int32_t G,
+                           int32_t Kp, int32_t pad, void* zg, hipStream_t s) {
   const int Tp = T + Kp;
   const int64_t nvec = (int64_t)G * B * Tp * (d / G) / 4;
   if (t == DType::F16)
-    hipLaunchKernelGGL(pos_pack_kernel<half_t>, dim3(grid_for(nvec)), dim3(256), 0, s, h, B, T, d, G, Tp, pad,
-                       (half_t*)zg, nvec);
+    hipLaunchKernelGGL(pos_pack_kernel<half_t>, dim3(grid_for(nvec)), dim3(256), 0, s, h, B, T, rows, d, G, Tp,
+                       pad, (half_t*)zg, nvec);
   else
-    hipLaunchKernelGGL(pos_pack_kernel<float>, dim3(grid_for(nvec)), dim3(256), 0, s, h, B, T, d, G, Tp, pad,
-                       (float*)zg, nvec);
+    hipLaunchKernelGGL(pos_pack_kernel<float>, dim3(grid_for(nvec)), dim3(256), 0, s, h, B, T, rows, d, G, Tp,
+                       pad, (float*)zg, nvec);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_tables(const RowTable* tabs, int32_t n, int32_t B, int32_t tmax, hipStream_t s) {
+  if (n < 1 || n > kMaxRowTables || B < 1 || tmax < 1) return hipErrorInvalidValue;
+  RowTables rt{};
+  for (int i = 0; i < n; ++i) rt.t[i] = tabs[i];
+  hipLaunchKernelGGL(row_tables_kernel, dim3((tmax + 255) / 256, B, n), dim3(256), 0, s, rt);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_tail_frames(float* y, int32_t B, int32_t T, int32_t V, const int32_t* len, hipStream_t s) {
+  const int64_t nvec = (int64_t)B * T * V;
+  hipLaunchKernelGGL(zero_tail_kernel, dim3(grid_for(nvec)), dim3(256), 0, s, y, B, T, V, len, nvec);
   return hipGetLastError();
 }
 

@@ -247,6 +247,26 @@ def main() -> int:
     roof["work_per_launch"] = per_launch
     roof["work_unit"] = kind
 
+    # true-length leg: the same rows, each computed as its own clip of its
+    # valid[b] samples (rows packed, work proportional to the valid audio);
+    # reported beside the padded-window metric, never as `value`
+    tl_logits = torch.empty_like(logits)
+
+    def tl_step():
+        model.forward_true_length(tp, valid, tl_logits, vf)
+        w2.ctc_greedy(tl_logits, vf, cfg.blank_id, ids, lens)
+
+    for _ in range(args.warmup):
+        tl_step()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        tl_step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    tl_ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] true-length mode: {tl_ms:.3f} ms/step", file=sys.stderr, flush=True)
+
     kernels = {}
     for k, (ms, n) in sorted(per_kernel.items(), key=lambda kv: -kv[1][0]):
         ent = {"ms_per_step": round(ms / prof_steps, 4), "launches_per_step": n // prof_steps}
@@ -270,6 +290,9 @@ def main() -> int:
                    "precision": "fp16 operands, fp32 accumulation/normalisation" if cfg.precision == "fp16"
                    else "fp32", "valid_audio_s": round(valid_s, 2)},
         "rtfx_valid_audio": round(valid_s / (ms_step / 1e3), 1),
+        "true_length": {"ms_per_step": round(tl_ms, 4), "valid_audio_sec_per_sec": round(valid_s / (tl_ms / 1e3), 1),
+                        "speedup_over_padded": round(ms_step / tl_ms, 3),
+                        "mode": "each row computed as its own clip of valid[b] samples, rows packed"},
         "wall_s_timed": round(t_wall, 3),
         "stages_ms": {"frontend": round(fe, 4), "encoder_head_ctc": round(enc, 4)},
         "kernels": kernels,

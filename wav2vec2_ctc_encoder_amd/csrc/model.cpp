@@ -249,7 +249,10 @@ struct w2v2_model {
   int32_t* tl_i32 = nullptr;  // true-length: [2 * n_conv + 1][max_batch] lengths, starts, valid
   int64_t* tl_base = nullptr; // [n_conv + 1][max_batch] table bases
   int64_t* tl_rows = nullptr; // per-row offset tables
-  std::vector<int64_t> tl_host;  // host copy of the int32 + int64 part, uploaded per call
+  int64_t* tl_pinned = nullptr;  // pinned host staging of the int32 + int64 part
+  size_t tl_bytes = 0;
+  hipEvent_t tl_copied = nullptr; // recorded after each upload from tl_pinned
+  bool tl_pending = false;
   double* gn_part = nullptr;
   float2* gn_ss = nullptr;
   float* h = nullptr;
@@ -261,6 +264,8 @@ struct w2v2_model {
 
   ~w2v2_model() {
     delete prof;
+    if (tl_copied) (void)hipEventDestroy(tl_copied);
+    if (tl_pinned) (void)hipHostFree(tl_pinned);
     if (wmem) (void)hipFree(wmem);
     if (ws) (void)hipFree(ws);
   }
@@ -843,14 +848,30 @@ w2v2_status w2v2_forward_true_length(w2v2_model* m, const float* pcm, const int3
   DeviceGuard guard(m->device);
   hipStream_t s = (hipStream_t)stream;
 
-  // host: frames and packed starts of every row at every conv level
+  // host: frames and packed starts of every row at every conv level, staged
+  // in pinned memory; the previous call's upload from it must have finished
   const int64_t words = tl_i32_words(c);
-  std::vector<int64_t>& blob = m->tl_host;
-  blob.assign((size_t)(words / 2 + (int64_t)(n + 1) * Bm), 0);
-  int32_t* len = (int32_t*)blob.data();              // [n][Bm]
+  const size_t nwords = (size_t)(words / 2 + (int64_t)(n + 1) * Bm);
+  if (!m->tl_pinned) {
+    if (hipHostMalloc((void**)&m->tl_pinned, nwords * sizeof(int64_t), hipHostMallocDefault) != hipSuccess) {
+      m->tl_pinned = nullptr;
+      return fail(W2V2_E_NOMEM, "cannot allocate pinned staging for the row lengths");
+    }
+    m->tl_bytes = nwords * sizeof(int64_t);
+    if (hipEventCreateWithFlags(&m->tl_copied, hipEventDisableTiming) != hipSuccess) {
+      m->tl_copied = nullptr;
+      return fail(W2V2_E_DEVICE, "hipEventCreate failed");
+    }
+  }
+  if (m->tl_pending && hipEventSynchronize(m->tl_copied) != hipSuccess)
+    return fail(W2V2_E_DEVICE, "waiting for the previous upload failed");
+  m->tl_pending = false;
+  int64_t* blob = m->tl_pinned;
+  std::memset(blob, 0, m->tl_bytes);
+  int32_t* len = (int32_t*)blob;                     // [n][Bm]
   int32_t* start = len + (size_t)n * Bm;             // [n][Bm]
   int32_t* vcopy = start + (size_t)n * Bm;           // [Bm]
-  int64_t* base = blob.data() + words / 2;           // [n + 1][Bm]
+  int64_t* base = blob + words / 2;                  // [n + 1][Bm]
   Packing pk;
   for (int b = 0; b < B; ++b) {
     vcopy[b] = valid_host[b];
@@ -879,10 +900,10 @@ w2v2_status w2v2_forward_true_length(w2v2_model* m, const float* pcm, const int3
     base[(size_t)(n - 1) * Bm + b] = (int64_t)b * (Tf + K) * Cg;
     base[(size_t)n * Bm + b] = (int64_t)b * Tf * c.vocab;
   }
-  // pageable source: the runtime stages it before returning, so the host
-  // block may be refilled by the next call
-  if (hipMemcpyAsync(m->tl_i32, blob.data(), blob.size() * sizeof(int64_t), hipMemcpyHostToDevice, s) != hipSuccess)
+  if (hipMemcpyAsync(m->tl_i32, blob, m->tl_bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipEventRecord(m->tl_copied, s) != hipSuccess)
     return fail(W2V2_E_DEVICE, "upload of the row lengths failed");
+  m->tl_pending = true;
 
   const int32_t* dlen = m->tl_i32;
   const int32_t* dstart = m->tl_i32 + (size_t)n * Bm;

@@ -230,9 +230,9 @@ w2v2_status w2v2_forward(w2v2_model* model, const float* pcm, const int32_t* val
  *              row b for t < w2v2_num_frames(valid[b]), 0 for later frames.
  *   vframes    dev int32 [batch] or NULL: w2v2_num_frames(valid[b]).
  * Asynchronous on `stream` like w2v2_forward: the lengths are copied into a
- * pinned staging buffer owned by the model (allocated on the first call) and
- * uploaded on that stream; a call first waits for the previous call's upload
- * from that buffer.  Calls that share a model must not overlap.
+ * pinned staging buffer that w2v2_create allocated and uploaded on that
+ * stream; a call first waits for the previous call's upload from that buffer.
+ * Allocates nothing.  Calls that share a model must not overlap.
  * Errors: W2V2_E_ARG (null model/pcm/valid_host/logits, batch out of range,
  * a valid[b] outside [0, window]), W2V2_E_DEVICE (copy or launch failure).
  */

@@ -788,6 +788,19 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
   m->tl_i32 = (int32_t*)(wsb + offs[10]);
   m->tl_base = (int64_t*)(wsb + offs[10] + (size_t)tl_i32_words(c) * 4);
   m->tl_rows = (int64_t*)(wsb + offs[11]);
+  // pinned staging of the true-length tables (lengths, starts, valid, bases)
+  m->tl_bytes = (size_t)tl_i32_words(c) * 4 + (size_t)(c.n_conv + 1) * Bm * 8;
+  if (hipHostMalloc((void**)&m->tl_pinned, m->tl_bytes, hipHostMallocDefault) != hipSuccess) {
+    m->tl_pinned = nullptr;
+    (void)hipGetLastError();
+    delete m;
+    return fail(W2V2_E_NOMEM, "cannot allocate pinned staging for the row lengths");
+  }
+  if (hipEventCreateWithFlags(&m->tl_copied, hipEventDisableTiming) != hipSuccess) {
+    m->tl_copied = nullptr;
+    delete m;
+    return fail(W2V2_E_DEVICE, "hipEventCreate failed");
+  }
   m->ffn = wsb + offs[8];
   m->zg = wsb + offs[9];
   if (hipDeviceSynchronize() != hipSuccess) {
@@ -851,18 +864,6 @@ w2v2_status w2v2_forward_true_length(w2v2_model* m, const float* pcm, const int3
   // host: frames and packed starts of every row at every conv level, staged
   // in pinned memory; the previous call's upload from it must have finished
   const int64_t words = tl_i32_words(c);
-  const size_t nwords = (size_t)(words / 2 + (int64_t)(n + 1) * Bm);
-  if (!m->tl_pinned) {
-    if (hipHostMalloc((void**)&m->tl_pinned, nwords * sizeof(int64_t), hipHostMallocDefault) != hipSuccess) {
-      m->tl_pinned = nullptr;
-      return fail(W2V2_E_NOMEM, "cannot allocate pinned staging for the row lengths");
-    }
-    m->tl_bytes = nwords * sizeof(int64_t);
-    if (hipEventCreateWithFlags(&m->tl_copied, hipEventDisableTiming) != hipSuccess) {
-      m->tl_copied = nullptr;
-      return fail(W2V2_E_DEVICE, "hipEventCreate failed");
-    }
-  }
   if (m->tl_pending && hipEventSynchronize(m->tl_copied) != hipSuccess)
     return fail(W2V2_E_DEVICE, "waiting for the previous upload failed");
   m->tl_pending = false;

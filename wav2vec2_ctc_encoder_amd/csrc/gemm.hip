@@ -11,18 +11,33 @@
 //  * the grouped positional conv, one grid.z slice per group, over a
 //    zero-padded per-group copy of its input (lda = C_g, K = taps*C_g).
 //
-// Tiling: 256 threads = 4 waves.  Block tile BM x BN, K step of 128 bytes
-// per row (64 fp16 / 32 fp32), double-buffered LDS with the next K step
-// prefetched into registers, one barrier per step.  Each wave owns a
-// (TN*16) x (TM*16) sub-tile built from 16x16 MFMA blocks.  The MFMA A
-// operand is the weight (n side) and the B operand the activation (m side),
-// so every lane ends up holding 4 consecutive output columns of one row and
-// the epilogue stores 16-byte (fp32) / 8-byte (fp16) vectors.
+// Two kernels, both 256 threads = 4 waves with the weight as the MFMA A
+// operand (n side) and the activation as the B operand (m side), so a lane
+// holds consecutive output columns of one row:
 //
-// fp16: v_mfma_f32_16x16x32_f16, one per 16-byte lane fragment.
-// fp32: v_mfma_f32_16x16x4_f32, four per 16-byte lane fragment; fragment
-//       element j of lane group g carries k = 4g + j for both operands, a
-//       permutation of the 16 k values, so the sum is unchanged.
+// gemm_dlds_kernel (fp16, K % 64 == 0, N > 32; the hot path): block tile
+//   128x128 or 128x64, waves 2 x 2, v_mfma_f32_32x32x16_f16.  K advances in
+//   64-wide steps through a two-stage LDS ring filled by wave-wide direct
+//   global->LDS loads (global_load_lds_dwordx4, 16 bytes per lane) into
+//   XOR-swizzled 128-byte rows; explicit vmcnt waits, one barrier per step,
+//   fragments double-buffered in registers with MFMAs and LDS reads
+//   interleaved.  Epilogue: bias and activation in registers, then each wave
+//   stages its 32-row slabs row-major in LDS and writes whole rows (residual
+//   add, fp32 and/or fp16 stores), because the 32x32 accumulator layout
+//   would otherwise scatter 16-byte pieces over 32 rows per store.
+//
+// gemm_kernel (fp32 mode and the remaining shapes): block tile BM x BN, K
+//   step of 128 bytes per row (64 fp16 / 32 fp32), double-buffered LDS with
+//   the next K step prefetched into registers, one barrier per step; each
+//   wave owns a (TN*16) x (TM*16) sub-tile of 16x16 MFMA blocks and stores
+//   16-byte (fp32) / 8-byte (fp16) vectors.
+//   fp16: v_mfma_f32_16x16x32_f16, one per 16-byte lane fragment.
+//   fp32: v_mfma_f32_16x16x4_f32, four per 16-byte lane fragment; fragment
+//         element j of lane group g carries k = 4g + j for both operands, a
+//         permutation of the 16 k values, so the sum is unchanged.
+//
+// A rows come from the segment rule above or, for packed true-length rows,
+// from a per-row offset table; output rows likewise (c_rows).
 #include "common.h"
 
 namespace w2v2 {

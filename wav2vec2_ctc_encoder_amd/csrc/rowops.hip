@@ -1,5 +1,7 @@
 // Row-wise and elementwise kernels: LayerNorm (+ optional GELU), the
-// zero-padded per-group packing that feeds the positional conv, and casts.
+// zero-padded per-group packing that feeds the positional conv, casts, and
+// the true-length helpers (packed-row offset tables, zeroing the logits of
+// frames past a row's own frames).
 //
 // LayerNorm: one wave per row, the row held in registers as float4 groups
 // (lane i takes elements 4i, 4i+256, ...), statistics in fp32 with wave

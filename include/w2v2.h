@@ -206,6 +206,12 @@ w2v2_status w2v2_model_info(const w2v2_model* model, int32_t* frames_per_window,
  *           with no mask.
  *   vframes dev int32 [batch] or NULL: frames to decode per row
  *           (w2v2_num_frames of valid[b], computed on the device).
+ * Execution: for batch >= 2 the two halves of the batch run concurrently,
+ * the first on `stream`, the second on a stream the model owns that is
+ * forked from and joined back to `stream` with events, so the call remains
+ * asynchronous and ordered on `stream`.  Results are bit-identical to a
+ * serial run (rows are independent).  While w2v2_profile_enable profiles
+ * every kernel (no filter), the whole batch runs as one pass on `stream`.
  * Errors: W2V2_E_ARG (null model/pcm/valid/logits, batch out of range),
  * W2V2_E_DEVICE (launch failure).
  */
@@ -280,9 +286,13 @@ w2v2_status w2v2_ctc_greedy(const float* logits, const int32_t* vframes, int32_t
 
 /*
  * Per-kernel timing with HIP events.  When enabled, the model's calls record
- * an event pair around every kernel they launch (on the caller's stream),
- * or, if `only` is not NULL, around the launches whose kernel name equals
- * `only` (so a timed loop can watch one kernel with two events per launch).
+ * an event pair around every kernel they launch (on the stream the kernel
+ * runs on), or, if `only` is not NULL, around the launches whose kernel name
+ * equals `only` (so a timed loop can watch one kernel with two events per
+ * launch).  Without `only`, w2v2_forward runs the whole batch as one pass
+ * on the caller's stream, so every timed kernel runs alone; with `only` it
+ * keeps the two halves concurrent, and a timed launch then shares the GPU
+ * with the other half's kernels.
  * w2v2_profile_read synchronizes on the recorded events, accumulates the
  * per-kernel-name totals since the last read, and writes up to `cap`
  * entries: names[i] (static strings owned by the library), total_ms[i] and

@@ -210,6 +210,16 @@ struct Profiler : LaunchHook {
 // ----------------------------------------------------------------------------
 // model
 // ----------------------------------------------------------------------------
+// Workspace regions of one forward (the whole batch, or one half of it).
+struct Ws {
+  void *bufA = nullptr, *bufB = nullptr;
+  double* gn_part = nullptr;
+  float2* gn_ss = nullptr;
+  float* h = nullptr;
+  void *x = nullptr, *qkv = nullptr, *attn = nullptr, *ffn = nullptr, *zg = nullptr;
+};
+constexpr int kWsRegions = 10;
+
 struct w2v2_model {
   w2v2_config cfg{};
   int device = 0;
@@ -244,8 +254,16 @@ struct w2v2_model {
   const void* head_w = nullptr;
   const float* head_b = nullptr;
 
-  // workspace regions
-  void *bufA = nullptr, *bufB = nullptr;
+  // workspace regions; row_bytes[i] is region i's share per batch row (in
+  // Ws field order), so rows [b0, b0 + n) of every region form a Ws of
+  // their own.  The positional-conv input [G][n][T + K][d/G] of such a
+  // slice is contiguous inside its share.
+  Ws w;
+  size_t row_bytes[kWsRegions] = {};
+  // second stream of w2v2_forward (one half of the batch runs there) and
+  // the events that fork it from and join it back to the caller's stream
+  hipStream_t aux = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   int32_t* tl_i32 = nullptr;  // true-length: [2 * n_conv + 1][max_batch] lengths, starts, valid
   int64_t* tl_base = nullptr; // [n_conv + 1][max_batch] table bases
   int64_t* tl_rows = nullptr; // per-row offset tables
@@ -253,10 +271,6 @@ struct w2v2_model {
   size_t tl_bytes = 0;
   hipEvent_t tl_copied = nullptr; // recorded after each upload from tl_pinned
   bool tl_pending = false;
-  double* gn_part = nullptr;
-  float2* gn_ss = nullptr;
-  float* h = nullptr;
-  void *x = nullptr, *qkv = nullptr, *attn = nullptr, *ffn = nullptr, *zg = nullptr;
 
   Profiler* prof = nullptr;
   bool prof_on = false;
@@ -264,6 +278,9 @@ struct w2v2_model {
 
   ~w2v2_model() {
     delete prof;
+    if (ev_fork) (void)hipEventDestroy(ev_fork);
+    if (ev_join) (void)hipEventDestroy(ev_join);
+    if (aux) (void)hipStreamDestroy(aux);
     if (tl_copied) (void)hipEventDestroy(tl_copied);
     if (tl_pinned) (void)hipHostFree(tl_pinned);
     if (wmem) (void)hipFree(wmem);
@@ -322,7 +339,7 @@ struct Packing {
 };
 
 // conv 0 .. n-1; returns the final conv output buffer in *feat
-w2v2_status run_frontend(w2v2_model* m, const float* pcm, const int32_t* valid, int B, hipStream_t s,
+w2v2_status run_frontend(w2v2_model* m, const Ws& w, const float* pcm, const int32_t* valid, int B, hipStream_t s,
                          const void** feat, const Packing* pk = nullptr) {
   const w2v2_config& c = m->cfg;
   const DType dt = m->dt;
@@ -331,24 +348,24 @@ w2v2_status run_frontend(w2v2_model* m, const float* pcm, const int32_t* valid, 
   if (c.feat_norm == W2V2_NORM_GROUP) {
     W2V2_LAUNCH(m, s, "gn0_stats",
                 launch_gn0_stats(pcm, valid, c.window, B, c.conv_kernel[0], c.conv_stride[0], m->T[0], rows0.len,
-                                 m->gn_part, s));
+                                 w.gn_part, s));
     W2V2_LAUNCH(m, s, "gn0_finalize",
-                launch_gn0_finalize(m->gn_part, B, c.conv_kernel[0], m->T[0], rows0.len, (const float*)m->conv[0].w,
-                                    m->conv[0].bias, C0, m->conv[0].gamma, m->conv[0].beta, c.eps, m->gn_ss, s));
+                launch_gn0_finalize(w.gn_part, B, c.conv_kernel[0], m->T[0], rows0.len, (const float*)m->conv[0].w,
+                                    m->conv[0].bias, C0, m->conv[0].gamma, m->conv[0].beta, c.eps, w.gn_ss, s));
     W2V2_LAUNCH(m, s, "conv0_gn_gelu",
                 launch_conv0(dt, pcm, valid, c.window, B, (const float*)m->conv[0].w, m->conv[0].bias, C0,
-                             c.conv_kernel[0], c.conv_stride[0], m->T[0], rows0, m->bufA, m->gn_ss, nullptr,
+                             c.conv_kernel[0], c.conv_stride[0], m->T[0], rows0, w.bufA, w.gn_ss, nullptr,
                              nullptr, c.eps, m->act, s));
   } else {
     W2V2_LAUNCH(m, s, "conv0_ln_gelu",
                 launch_conv0(dt, pcm, valid, c.window, B, (const float*)m->conv[0].w, m->conv[0].bias, C0,
-                             c.conv_kernel[0], c.conv_stride[0], m->T[0], rows0, m->bufA, nullptr,
+                             c.conv_kernel[0], c.conv_stride[0], m->T[0], rows0, w.bufA, nullptr,
                              m->conv[0].gamma, m->conv[0].beta, c.eps, m->act, s));
   }
-  const void* cur = m->bufA;
+  const void* cur = w.bufA;
   int tin = m->T[0], cin = C0;
   for (int i = 1; i < c.n_conv; ++i) {
-    void* out = (i & 1) ? m->bufB : m->bufA;
+    void* out = (i & 1) ? w.bufB : w.bufA;
     GemmArgs g;
     g.role = kGemmConv;
     g.A = cur;
@@ -409,7 +426,7 @@ w2v2_status gemm_linear(w2v2_model* m, hipStream_t s, const char* name, int role
     if (st_ != W2V2_OK) return st_;     \
   } while (0)
 
-w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, hipStream_t s,
+w2v2_status run_encoder(w2v2_model* m, const Ws& w, const void* feat, int B, float* logits, hipStream_t s,
                         const Packing* pk = nullptr) {
   const w2v2_config& c = m->cfg;
   const DType dt = m->dt;
@@ -421,16 +438,16 @@ w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, h
 
   // feature projection: LN over channels, then Linear C -> d (fp32 residual stream)
   W2V2_LAUNCH(m, s, "layernorm",
-              launch_layernorm(dt, nullptr, feat, M, cl, m->fp_g, m->fp_b, eps, nullptr, m->x, 0, s));
-  W2V2_TRY(gemm_linear(m, s, "gemm_feature_proj", kGemmProj, m->x, M, d, cl, m->fp_w, m->fp_bias, 0, nullptr, m->h, nullptr, d));
+              launch_layernorm(dt, nullptr, feat, M, cl, m->fp_g, m->fp_b, eps, nullptr, w.x, 0, s));
+  W2V2_TRY(gemm_linear(m, s, "gemm_feature_proj", kGemmProj, w.x, M, d, cl, m->fp_w, m->fp_bias, 0, nullptr, w.h, nullptr, d));
 
   // positional conv: h = z + GELU(posconv(z) + bias)
   const int pad = K / 2;
-  W2V2_LAUNCH(m, s, "pos_pack", launch_pos_pack(dt, m->h, B, T, rows, d, G, K, pad, m->zg, s));
+  W2V2_LAUNCH(m, s, "pos_pack", launch_pos_pack(dt, w.h, B, T, rows, d, G, K, pad, w.zg, s));
   {
     GemmArgs g;
     g.role = kGemmPos;
-    g.A = m->zg;
+    g.A = w.zg;
     g.lda = Cg;
     g.a_seg = (int64_t)(T + K) * Cg;
     g.seg_rows = T;
@@ -445,8 +462,8 @@ w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, h
     g.bias = m->pos_bias;
     g.bias_group = Cg;
     g.act = m->act;
-    g.residual = m->h;
-    g.out_f32 = m->h;
+    g.residual = w.h;
+    g.out_f32 = w.h;
     g.ldc = d;
     g.c_group = Cg;
     W2V2_LAUNCH(m, s, "pos_conv_gemm", launch_gemm(dt, g, s));
@@ -454,33 +471,33 @@ w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, h
   const bool stable = c.stable_layer_norm != 0;
   if (!stable)
     W2V2_LAUNCH(m, s, "layernorm",
-                launch_layernorm(dt, m->h, nullptr, M, d, m->enc_g, m->enc_b, eps, m->h, m->x, 0, s));
+                launch_layernorm(dt, w.h, nullptr, M, d, m->enc_g, m->enc_b, eps, w.h, w.x, 0, s));
 
   for (int l = 0; l < c.layers; ++l) {
     const w2v2_model::Layer& L = m->layers[l];
     if (stable)
       W2V2_LAUNCH(m, s, "layernorm",
-                  launch_layernorm(dt, m->h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, nullptr, m->x, 0, s));
-    W2V2_TRY(gemm_linear(m, s, "gemm_qkv", kGemmQKV, m->x, M, 3 * d, d, L.wqkv, L.bqkv, 0, nullptr, nullptr, m->qkv, 3 * d));
-    W2V2_LAUNCH(m, s, "attention", launch_attention(dt, m->qkv, m->attn, B, T, rows, c.heads, d / c.heads, s));
-    W2V2_TRY(gemm_linear(m, s, "gemm_out_proj", kGemmOut, m->attn, M, d, d, L.wo, L.bo, 0, m->h, m->h, nullptr, d));
+                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, nullptr, w.x, 0, s));
+    W2V2_TRY(gemm_linear(m, s, "gemm_qkv", kGemmQKV, w.x, M, 3 * d, d, L.wqkv, L.bqkv, 0, nullptr, nullptr, w.qkv, 3 * d));
+    W2V2_LAUNCH(m, s, "attention", launch_attention(dt, w.qkv, w.attn, B, T, rows, c.heads, d / c.heads, s));
+    W2V2_TRY(gemm_linear(m, s, "gemm_out_proj", kGemmOut, w.attn, M, d, d, L.wo, L.bo, 0, w.h, w.h, nullptr, d));
     if (stable)
       W2V2_LAUNCH(m, s, "layernorm",
-                  launch_layernorm(dt, m->h, nullptr, M, d, L.ln2_g, L.ln2_b, eps, nullptr, m->x, 0, s));
+                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln2_g, L.ln2_b, eps, nullptr, w.x, 0, s));
     else
       W2V2_LAUNCH(m, s, "layernorm",
-                  launch_layernorm(dt, m->h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, m->h, m->x, 0, s));
-    W2V2_TRY(gemm_linear(m, s, "gemm_ffn1", kGemmFFN1, m->x, M, F, d, L.w1, L.b1, m->act, nullptr, nullptr, m->ffn, F));
-    W2V2_TRY(gemm_linear(m, s, "gemm_ffn2", kGemmFFN2, m->ffn, M, d, F, L.w2, L.b2, 0, m->h, m->h, nullptr, d));
+                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, w.h, w.x, 0, s));
+    W2V2_TRY(gemm_linear(m, s, "gemm_ffn1", kGemmFFN1, w.x, M, F, d, L.w1, L.b1, m->act, nullptr, nullptr, w.ffn, F));
+    W2V2_TRY(gemm_linear(m, s, "gemm_ffn2", kGemmFFN2, w.ffn, M, d, F, L.w2, L.b2, 0, w.h, w.h, nullptr, d));
     if (!stable)
       W2V2_LAUNCH(m, s, "layernorm",
-                  launch_layernorm(dt, m->h, nullptr, M, d, L.ln2_g, L.ln2_b, eps, m->h, m->x, 0, s));
+                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln2_g, L.ln2_b, eps, w.h, w.x, 0, s));
   }
   if (stable)
     W2V2_LAUNCH(m, s, "layernorm",
-                launch_layernorm(dt, m->h, nullptr, M, d, m->enc_g, m->enc_b, eps, nullptr, m->x, 0, s));
+                launch_layernorm(dt, w.h, nullptr, M, d, m->enc_g, m->enc_b, eps, nullptr, w.x, 0, s));
   if (!pk) {
-    W2V2_TRY(gemm_linear(m, s, "gemm_ctc_head", kGemmHead, m->x, M, c.vocab, d, m->head_w, m->head_b, 0, nullptr,
+    W2V2_TRY(gemm_linear(m, s, "gemm_ctc_head", kGemmHead, w.x, M, c.vocab, d, m->head_w, m->head_b, 0, nullptr,
                          logits, nullptr, c.vocab));
     return W2V2_OK;
   }
@@ -488,7 +505,7 @@ w2v2_status run_encoder(w2v2_model* m, const void* feat, int B, float* logits, h
   // row's own frames are zero
   GemmArgs g;
   g.role = kGemmHead;
-  g.A = m->x;
+  g.A = w.x;
   g.lda = d;
   g.seg_rows = M > 0 ? M : 1;
   g.B = m->head_w;
@@ -777,14 +794,27 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
     return fail(W2V2_E_NOMEM, "cannot allocate " + std::to_string(total) + " bytes of workspace");
   }
   uint8_t* wsb = (uint8_t*)m->ws;
-  m->bufA = wsb + offs[0];
-  m->bufB = wsb + offs[1];
-  m->gn_part = (double*)(wsb + offs[2]);
-  m->gn_ss = (float2*)(wsb + offs[3]);
-  m->h = (float*)(wsb + offs[4]);
-  m->x = wsb + offs[5];
-  m->qkv = wsb + offs[6];
-  m->attn = wsb + offs[7];
+  m->w.bufA = wsb + offs[0];
+  m->w.bufB = wsb + offs[1];
+  m->w.gn_part = (double*)(wsb + offs[2]);
+  m->w.gn_ss = (float2*)(wsb + offs[3]);
+  m->w.h = (float*)(wsb + offs[4]);
+  m->w.x = wsb + offs[5];
+  m->w.qkv = wsb + offs[6];
+  m->w.attn = wsb + offs[7];
+  m->w.ffn = wsb + offs[8];
+  m->w.zg = wsb + offs[9];
+  for (int i = 0; i < kWsRegions; ++i) m->row_bytes[i] = sizes[i] / (size_t)Bm;
+  if (hipStreamCreateWithFlags(&m->aux, hipStreamNonBlocking) != hipSuccess) {
+    m->aux = nullptr;
+    delete m;
+    return fail(W2V2_E_DEVICE, "hipStreamCreate failed");
+  }
+  if (hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming) != hipSuccess) {
+    delete m;
+    return fail(W2V2_E_DEVICE, "hipEventCreate failed");
+  }
   m->tl_i32 = (int32_t*)(wsb + offs[10]);
   m->tl_base = (int64_t*)(wsb + offs[10] + (size_t)tl_i32_words(c) * 4);
   m->tl_rows = (int64_t*)(wsb + offs[11]);
@@ -801,8 +831,6 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
     delete m;
     return fail(W2V2_E_DEVICE, "hipEventCreate failed");
   }
-  m->ffn = wsb + offs[8];
-  m->zg = wsb + offs[9];
   if (hipDeviceSynchronize() != hipSuccess) {
     delete m;
     return fail(W2V2_E_DEVICE, "device synchronization failed after weight upload");
@@ -835,14 +863,59 @@ w2v2_status w2v2_model_info(const w2v2_model* m, int32_t* frames_per_window, int
   return W2V2_OK;
 }
 
+// Rows [b0, b0 + n) of every workspace region, as a workspace of its own.
+Ws ws_rows(const w2v2_model* m, int b0) {
+  auto at = [&](void* p, int i) { return (void*)((uint8_t*)p + (size_t)b0 * m->row_bytes[i]); };
+  Ws r;
+  r.bufA = at(m->w.bufA, 0);
+  r.bufB = at(m->w.bufB, 1);
+  r.gn_part = (double*)at(m->w.gn_part, 2);
+  r.gn_ss = (float2*)at(m->w.gn_ss, 3);
+  r.h = (float*)at(m->w.h, 4);
+  r.x = at(m->w.x, 5);
+  r.qkv = at(m->w.qkv, 6);
+  r.attn = at(m->w.attn, 7);
+  r.ffn = at(m->w.ffn, 8);
+  r.zg = at(m->w.zg, 9);
+  return r;
+}
+
+// Whole network on rows [b0, b0 + n) of the batch, on stream s.
+w2v2_status forward_rows(w2v2_model* m, const float* pcm, const int32_t* valid, int b0, int n, float* logits,
+                         hipStream_t s) {
+  const Ws w = ws_rows(m, b0);
+  const void* feat = nullptr;
+  W2V2_TRY(run_frontend(m, w, pcm + (size_t)b0 * m->cfg.window, valid + b0, n, s, &feat));
+  return run_encoder(m, w, feat, n, logits + (size_t)b0 * m->Tf * m->cfg.vocab, s);
+}
+
 w2v2_status w2v2_forward(w2v2_model* m, const float* pcm, const int32_t* valid, int32_t batch, float* logits,
                          int32_t* vframes, void* stream) {
   W2V2_TRY(check_forward_args(m, pcm, valid, batch, logits));
   DeviceGuard guard(m->device);
   hipStream_t s = (hipStream_t)stream;
-  const void* feat = nullptr;
-  W2V2_TRY(run_frontend(m, pcm, valid, batch, s, &feat));
-  W2V2_TRY(run_encoder(m, feat, batch, logits, s));
+  // profiling every kernel (no filter) runs the batch as one pass, so that each
+  // kernel's event-timed duration is its own and not shared with the other half
+  const bool serial = batch == 1 || (m->prof_on && m->prof_only.empty());
+  if (serial) {
+    W2V2_TRY(forward_rows(m, pcm, valid, 0, batch, logits, s));
+  } else {
+    // The two halves of the batch run concurrently, the first on the
+    // caller's stream and the second on the model's own stream, so that one
+    // half's latency-bound kernels (attention, norms, GEMM tails) overlap
+    // the other half's work.  Rows are independent: the results are the
+    // bits of a single-stream run.
+    const int b1 = (batch + 1) / 2;
+    if (hipEventRecord(m->ev_fork, s) != hipSuccess || hipStreamWaitEvent(m->aux, m->ev_fork, 0) != hipSuccess)
+      return fail(W2V2_E_DEVICE, "fork of the second stream failed");
+    w2v2_status st0 = forward_rows(m, pcm, valid, 0, b1, logits, s);
+    w2v2_status st1 = st0 == W2V2_OK ? forward_rows(m, pcm, valid, b1, batch - b1, logits, m->aux) : st0;
+    // the caller's stream waits for the second half whatever happened
+    if (hipEventRecord(m->ev_join, m->aux) != hipSuccess || hipStreamWaitEvent(s, m->ev_join, 0) != hipSuccess)
+      return fail(W2V2_E_DEVICE, "join of the second stream failed");
+    if (st0 != W2V2_OK) return st0;
+    if (st1 != W2V2_OK) return st1;
+  }
   if (vframes)
     W2V2_LAUNCH(m, s, "valid_frames",
                 launch_valid_frames(valid, batch, m->cfg.window, m->cfg.n_conv, m->cfg.conv_kernel,
@@ -935,8 +1008,8 @@ w2v2_status w2v2_forward_true_length(w2v2_model* m, const float* pcm, const int3
   W2V2_LAUNCH(m, s, "row_tables", launch_row_tables(tabs, nt, B, tmax, s));
 
   const void* feat = nullptr;
-  W2V2_TRY(run_frontend(m, pcm, dvalid, B, s, &feat, &pk));
-  W2V2_TRY(run_encoder(m, feat, B, logits, s, &pk));
+  W2V2_TRY(run_frontend(m, m->w, pcm, dvalid, B, s, &feat, &pk));
+  W2V2_TRY(run_encoder(m, m->w, feat, B, logits, s, &pk));
   if (vframes)
     W2V2_LAUNCH(m, s, "valid_frames",
                 launch_valid_frames(dvalid, B, c.window, c.n_conv, c.conv_kernel, c.conv_stride, vframes, s));
@@ -949,7 +1022,7 @@ w2v2_status w2v2_forward_frontend(w2v2_model* m, const float* pcm, const int32_t
   DeviceGuard guard(m->device);
   hipStream_t s = (hipStream_t)stream;
   const void* feat = nullptr;
-  W2V2_TRY(run_frontend(m, pcm, valid, batch, s, &feat));
+  W2V2_TRY(run_frontend(m, m->w, pcm, valid, batch, s, &feat));
   const int64_t n = (int64_t)batch * m->Tf * m->cfg.conv_dim[m->cfg.n_conv - 1];
   W2V2_LAUNCH(m, s, "cast_to_f32", launch_cast_to_f32(m->dt, feat, features, n, s));
   return W2V2_OK;
@@ -961,8 +1034,8 @@ w2v2_status w2v2_forward_encoder(w2v2_model* m, const float* features, int32_t b
   DeviceGuard guard(m->device);
   hipStream_t s = (hipStream_t)stream;
   const int64_t n = (int64_t)batch * m->Tf * m->cfg.conv_dim[m->cfg.n_conv - 1];
-  W2V2_LAUNCH(m, s, "cast_from_f32", launch_cast_from_f32(m->dt, features, m->bufA, n, s));
-  W2V2_TRY(run_encoder(m, m->bufA, batch, logits, s));
+  W2V2_LAUNCH(m, s, "cast_from_f32", launch_cast_from_f32(m->dt, features, m->w.bufA, n, s));
+  W2V2_TRY(run_encoder(m, m->w, m->w.bufA, batch, logits, s));
   return W2V2_OK;
 }
 

@@ -345,3 +345,23 @@ def test_deterministic_and_batch_permutation():
         # a smaller batch in the same model gives the same rows
         d, _ = m.forward(tp[:3].contiguous(), tv[:3].contiguous())
         assert torch.equal(d, a[:3])
+
+
+@pytest.mark.parametrize("batch", [2, 5])
+def test_two_stream_split_matches_one_pass(batch):
+    # batch >= 2 runs its halves concurrently on two streams; profiling every
+    # kernel runs it as one pass on one stream: the bits must agree
+    import wav2vec2_ctc_encoder_amd as w2
+    cfg = synth.BASE_10S_B1.replace(batch=batch, layers=2, valid_range=(20000, 160000), pcm_seed=4242)
+    _say(f"two-stream split vs one pass, batch {batch}")
+    W, pcm, valid = _inputs(cfg)
+    with w2.Model(cfg, W, max_batch=batch) as m:
+        tp, tv = torch.from_numpy(pcm).cuda(), torch.from_numpy(valid).cuda()
+        split, vf_split = m.forward(tp, tv)
+        m.profile_enable(True)
+        one, vf_one = m.forward(tp, tv)
+        torch.cuda.synchronize()
+        m.profile_read()
+        m.profile_enable(False)
+        assert torch.equal(vf_split, vf_one)
+        assert torch.equal(split, one)

@@ -593,10 +593,11 @@ hipError_t launch_shape(const GemmArgs& a, hipStream_t s) {
     if (a.K % 64 == 0 && a.N > 32) {
       const int64_t tiles128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.groups;
       // 128x128 tiles read less per MFMA and win on the 512-wide conv GEMMs
-      // and wherever there are enough of them to keep two per CU busy for a
-      // few rounds; with fewer tiles (N = 768 at M ~ 6400, or the M ~ 3200
-      // shapes) 128x64 tiles balance the CUs better.  Measured on gfx950.
-      if (a.N > 64 && (a.N <= 512 || tiles128 >= 850)) return launch_dlds<128, 128, 2, 128, ROLE>(a, s);
+      // and wherever there are at least ~400 of them; with fewer (N = 768
+      // linears: out-proj, FFN2, projection) 128x64 tiles balance the CUs
+      // better.  The threshold was measured with the two batch halves of a
+      // forward running concurrently (half-batch FFN1 / QKV: M = 3196).
+      if (a.N > 64 && (a.N <= 512 || tiles128 >= 400)) return launch_dlds<128, 128, 2, 128, ROLE>(a, s);
       return launch_dlds<128, 64, 2, 128, ROLE>(a, s);
     }
   }

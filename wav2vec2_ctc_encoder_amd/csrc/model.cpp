@@ -219,6 +219,9 @@ struct Ws {
   void *x = nullptr, *qkv = nullptr, *attn = nullptr, *ffn = nullptr, *zg = nullptr;
 };
 constexpr int kWsRegions = 10;
+// w2v2_forward splits a batch into up to kSplit row ranges that run
+// concurrently, one per stream (the caller's and kSplit - 1 of the model's).
+constexpr int kSplit = 2;
 
 struct w2v2_model {
   w2v2_config cfg{};
@@ -260,10 +263,11 @@ struct w2v2_model {
   // slice is contiguous inside its share.
   Ws w;
   size_t row_bytes[kWsRegions] = {};
-  // second stream of w2v2_forward (one half of the batch runs there) and
-  // the events that fork it from and join it back to the caller's stream
-  hipStream_t aux = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  // the model's own streams of w2v2_forward (parts 1 .. kSplit-1 of the
+  // batch run there) and the events that fork them from and join them back
+  // to the caller's stream
+  hipStream_t aux[kSplit] = {};
+  hipEvent_t ev_fork = nullptr, ev_join[kSplit] = {};
   int32_t* tl_i32 = nullptr;  // true-length: [2 * n_conv + 1][max_batch] lengths, starts, valid
   int64_t* tl_base = nullptr; // [n_conv + 1][max_batch] table bases
   int64_t* tl_rows = nullptr; // per-row offset tables
@@ -279,8 +283,10 @@ struct w2v2_model {
   ~w2v2_model() {
     delete prof;
     if (ev_fork) (void)hipEventDestroy(ev_fork);
-    if (ev_join) (void)hipEventDestroy(ev_join);
-    if (aux) (void)hipStreamDestroy(aux);
+    for (int i = 0; i < kSplit; ++i) {
+      if (ev_join[i]) (void)hipEventDestroy(ev_join[i]);
+      if (aux[i]) (void)hipStreamDestroy(aux[i]);
+    }
     if (tl_copied) (void)hipEventDestroy(tl_copied);
     if (tl_pinned) (void)hipHostFree(tl_pinned);
     if (wmem) (void)hipFree(wmem);
@@ -805,15 +811,22 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
   m->w.ffn = wsb + offs[8];
   m->w.zg = wsb + offs[9];
   for (int i = 0; i < kWsRegions; ++i) m->row_bytes[i] = sizes[i] / (size_t)Bm;
-  if (hipStreamCreateWithFlags(&m->aux, hipStreamNonBlocking) != hipSuccess) {
-    m->aux = nullptr;
-    delete m;
-    return fail(W2V2_E_DEVICE, "hipStreamCreate failed");
-  }
-  if (hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming) != hipSuccess) {
+  if (hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming) != hipSuccess) {
+    m->ev_fork = nullptr;
     delete m;
     return fail(W2V2_E_DEVICE, "hipEventCreate failed");
+  }
+  for (int i = 1; i < kSplit; ++i) {
+    if (hipStreamCreateWithFlags(&m->aux[i], hipStreamNonBlocking) != hipSuccess) {
+      m->aux[i] = nullptr;
+      delete m;
+      return fail(W2V2_E_DEVICE, "hipStreamCreate failed");
+    }
+    if (hipEventCreateWithFlags(&m->ev_join[i], hipEventDisableTiming) != hipSuccess) {
+      m->ev_join[i] = nullptr;
+      delete m;
+      return fail(W2V2_E_DEVICE, "hipEventCreate failed");
+    }
   }
   m->tl_i32 = (int32_t*)(wsb + offs[10]);
   m->tl_base = (int64_t*)(wsb + offs[10] + (size_t)tl_i32_words(c) * 4);
@@ -900,21 +913,28 @@ w2v2_status w2v2_forward(w2v2_model* m, const float* pcm, const int32_t* valid, 
   if (serial) {
     W2V2_TRY(forward_rows(m, pcm, valid, 0, batch, logits, s));
   } else {
-    // The two halves of the batch run concurrently, the first on the
-    // caller's stream and the second on the model's own stream, so that one
-    // half's latency-bound kernels (attention, norms, GEMM tails) overlap
-    // the other half's work.  Rows are independent: the results are the
-    // bits of a single-stream run.
-    const int b1 = (batch + 1) / 2;
-    if (hipEventRecord(m->ev_fork, s) != hipSuccess || hipStreamWaitEvent(m->aux, m->ev_fork, 0) != hipSuccess)
-      return fail(W2V2_E_DEVICE, "fork of the second stream failed");
-    w2v2_status st0 = forward_rows(m, pcm, valid, 0, b1, logits, s);
-    w2v2_status st1 = st0 == W2V2_OK ? forward_rows(m, pcm, valid, b1, batch - b1, logits, m->aux) : st0;
-    // the caller's stream waits for the second half whatever happened
-    if (hipEventRecord(m->ev_join, m->aux) != hipSuccess || hipStreamWaitEvent(s, m->ev_join, 0) != hipSuccess)
-      return fail(W2V2_E_DEVICE, "join of the second stream failed");
-    if (st0 != W2V2_OK) return st0;
-    if (st1 != W2V2_OK) return st1;
+    // The batch is cut into np near-equal row ranges that run concurrently,
+    // the first on the caller's stream and the others on the model's own
+    // streams, so that one part's latency-bound kernels (attention, norms,
+    // GEMM tails) overlap the other parts' work.  Rows are independent: the
+    // results are the bits of a single-stream run.
+    const int np = std::min(batch, kSplit);
+    if (hipEventRecord(m->ev_fork, s) != hipSuccess) return fail(W2V2_E_DEVICE, "fork of the streams failed");
+    for (int p = 1; p < np; ++p)
+      if (hipStreamWaitEvent(m->aux[p], m->ev_fork, 0) != hipSuccess)
+        return fail(W2V2_E_DEVICE, "fork of the streams failed");
+    w2v2_status st = W2V2_OK;
+    int b0 = 0;
+    for (int p = 0; p < np && st == W2V2_OK; ++p) {
+      const int n = batch / np + (p < batch % np ? 1 : 0);
+      st = forward_rows(m, pcm, valid, b0, n, logits, p == 0 ? s : m->aux[p]);
+      b0 += n;
+    }
+    // the caller's stream waits for every part whatever happened
+    for (int p = 1; p < np; ++p)
+      if (hipEventRecord(m->ev_join[p], m->aux[p]) != hipSuccess || hipStreamWaitEvent(s, m->ev_join[p], 0) != hipSuccess)
+        return fail(W2V2_E_DEVICE, "join of the streams failed");
+    if (st != W2V2_OK) return st;
   }
   if (vframes)
     W2V2_LAUNCH(m, s, "valid_frames",

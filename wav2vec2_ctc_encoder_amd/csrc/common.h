@@ -95,6 +95,13 @@ struct GemmArgs {
   const float* bias = nullptr;
   int64_t bias_group = 0;
   const float* residual = nullptr;  // fp32, indexed like C; may alias out_f32
+  // Optional LayerNorm applied to the residual as it is read: residual
+  // element (m, n) is taken as (r - st.x) * st.y * res_gamma[n] + res_beta[n]
+  // with st = res_stats[m] = (mean, rstd) of row m (post-norm blocks keep the
+  // raw residual sum in memory and only its row statistics).
+  const float2* res_stats = nullptr;
+  const float* res_gamma = nullptr;
+  const float* res_beta = nullptr;
   float* out_f32 = nullptr;
   void* out_t = nullptr;
   int64_t ldc = 0, c_group = 0;
@@ -142,11 +149,11 @@ hipError_t launch_gn0_finalize(double* part, int32_t B, int32_t k, int32_t T0, c
 // ----------------------------------------------------------------------------
 // LayerNorm over the C entries of each of R rows.  Input fp32 (x_f32) or the
 // operand type (x_t); outputs fp32 (y_f32) and/or operand type (y_t); act 1
-// (erf GELU) or 2 (tanh GELU) is applied after the affine map.  Input and
-// output may alias.
+// (erf GELU) or 2 (tanh GELU) is applied after the affine map; stats, if
+// not null, receives (mean, rstd) per row.  Input and output may alias.
 hipError_t launch_layernorm(DType t, const float* x_f32, const void* x_t, int64_t R, int32_t C,
                             const float* gamma, const float* beta, float eps, float* y_f32,
-                            void* y_t, int32_t act, hipStream_t s);
+                            void* y_t, int32_t act, float2* stats, hipStream_t s);
 // Positional-conv input: h fp32 [B, T, d] -> zg [G][B][T + K][d/G] (operand
 // type) with `pad` zero frames before the data and zeros after it.  With
 // rows set, h holds packed rows (row b's frame t at rows.start[b] + t) and

@@ -82,10 +82,34 @@ __device__ inline int xcd_remap(int pid, int nb) {
   return x * per + (x < rem ? x : rem) + local;
 }
 
+// Residual element(s) of logical row m. With res_stats set, the residual
+// buffer holds a raw sum whose LayerNorm (row statistics res_stats[m], affine
+// res_gamma/res_beta) is applied here as it is read.
+__device__ inline float4 residual4(const GemmArgs& a, int m, int n, const float* r) {
+  float4 v = *(const float4*)r;
+  if (a.res_stats) {
+    const float2 st = a.res_stats[m];
+    const float4 g = *(const float4*)(a.res_gamma + n), b = *(const float4*)(a.res_beta + n);
+    v.x = (v.x - st.x) * st.y * g.x + b.x;
+    v.y = (v.y - st.x) * st.y * g.y + b.y;
+    v.z = (v.z - st.x) * st.y * g.z + b.z;
+    v.w = (v.w - st.x) * st.y * g.w + b.w;
+  }
+  return v;
+}
+__device__ inline float residual1(const GemmArgs& a, int m, int n, float r) {
+  if (a.res_stats) {
+    const float2 st = a.res_stats[m];
+    r = (r - st.x) * st.y * a.res_gamma[n] + a.res_beta[n];
+  }
+  return r;
+}
+
 // Epilogue for 4 consecutive output columns nb..nb+3 of row m:
 // v = acc + bias; v = act(v); v += residual; store fp32 and/or operand type.
 template <typename T, int ACT>
-__device__ inline void epilogue4(const GemmArgs& a, const float* bias, int64_t rowoff, int nb, f4 v, bool vec) {
+__device__ inline void epilogue4(const GemmArgs& a, const float* bias, int m, int64_t rowoff, int nb, f4 v,
+                                 bool vec) {
   if (vec) {
     if (bias) {
       const float4 bb = *(const float4*)(bias + nb);
@@ -93,7 +117,7 @@ __device__ inline void epilogue4(const GemmArgs& a, const float* bias, int64_t r
     }
     v.x = act_fn<ACT>(v.x); v.y = act_fn<ACT>(v.y); v.z = act_fn<ACT>(v.z); v.w = act_fn<ACT>(v.w);
     if (a.residual) {
-      const float4 rr = *(const float4*)(a.residual + rowoff + nb);
+      const float4 rr = residual4(a, m, nb, a.residual + rowoff + nb);
       v.x += rr.x; v.y += rr.y; v.z += rr.z; v.w += rr.w;
     }
     if (a.out_f32) *(float4*)(a.out_f32 + rowoff + nb) = make_float4(v.x, v.y, v.z, v.w);
@@ -113,7 +137,7 @@ __device__ inline void epilogue4(const GemmArgs& a, const float* bias, int64_t r
       float x = v[r];
       if (bias) x += bias[n];
       x = act_fn<ACT>(x);
-      if (a.residual) x += a.residual[rowoff + n];
+      if (a.residual) x += residual1(a, m, n, a.residual[rowoff + n]);
       if (a.out_f32) a.out_f32[rowoff + n] = x;
       if (a.out_t) ((T*)a.out_t)[rowoff + n] = (T)x;
     }
@@ -145,7 +169,8 @@ typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 // Whole 8-column chunks everywhere: the staged epilogue below stores 16 B of
 // fp16 (32 B of fp32) per lane.
 __device__ inline bool epilogue_staged_ok(const GemmArgs& a) {
-  const uintptr_t ptrs = (uintptr_t)a.out_t | (uintptr_t)a.out_f32 | (uintptr_t)a.residual | (uintptr_t)a.bias;
+  const uintptr_t ptrs = (uintptr_t)a.out_t | (uintptr_t)a.out_f32 | (uintptr_t)a.residual | (uintptr_t)a.bias |
+                         (uintptr_t)a.res_gamma | (uintptr_t)a.res_beta;
   return ((a.ldc & 7) == 0) && ((a.N & 7) == 0) && ((a.c_group & 7) == 0) && ((a.bias_group & 7) == 0) &&
          ((ptrs & 15) == 0);
 }
@@ -197,7 +222,7 @@ __device__ inline void epilogue_staged(const GemmArgs& a, f16x (&acc)[TN][TM], f
       if (m < a.M && n < a.N) {
         const int64_t off = cg + c_row_offset(a, m) + n;
         if (a.residual) {
-          const float4 r0 = *(const float4*)(a.residual + off), r1 = *(const float4*)(a.residual + off + 4);
+          const float4 r0 = residual4(a, m, n, a.residual + off), r1 = residual4(a, m, n + 4, a.residual + off + 4);
           x0.x += r0.x; x0.y += r0.y; x0.z += r0.z; x0.w += r0.w;
           x1.x += r1.x; x1.y += r1.y; x1.z += r1.z; x1.w += r1.w;
         }
@@ -346,7 +371,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
         const int nb = n0 + wn * TN * 16 + i * 16 + lg * 4;
-        if (nb < a.N) epilogue4<T, ACT>(a, bias, rowoff, nb, acc[i][j], vec);
+        if (nb < a.N) epilogue4<T, ACT>(a, bias, m, rowoff, nb, acc[i][j], vec);
       }
     }
   };
@@ -560,7 +585,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dlds_kernel(GemmArgs a) {
           const int nb = n0 + wn * TN * 32 + i * 32 + 8 * q + 4 * lg;
           if (nb < a.N) {
             const f4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            epilogue4<half_t, ACT>(a, bias, rowoff, nb, v, vec);
+            epilogue4<half_t, ACT>(a, bias, m, rowoff, nb, v, vec);
           }
         }
       }

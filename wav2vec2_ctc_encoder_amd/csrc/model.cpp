@@ -11,7 +11,9 @@
 // Data layout in device memory (channels-last throughout):
 //   conv i output        [B, T_i, C_i]   operand type, ping-pong buffers A/B
 //   GroupNorm partials   [B, chunks, k + k(k+1)/2] fp64 (input lag statistics)
-//   residual stream h    [B*T, d]        fp32
+//   residual stream h    [B*T, d]        fp32 (post-norm: the raw residual sum,
+//                                        normalised by its reader; see run_encoder)
+//   LayerNorm row stats  [B*T] (mean, rstd) fp32
 //   GEMM operand x       [B*T, max(d, C_last)]  operand type (LayerNorm output)
 //   qkv                  [B*T, 3d]       operand type
 //   attention out        [B*T, d]        operand type
@@ -217,8 +219,9 @@ struct Ws {
   float2* gn_ss = nullptr;
   float* h = nullptr;
   void *x = nullptr, *qkv = nullptr, *attn = nullptr, *ffn = nullptr, *zg = nullptr;
+  float2* lnst = nullptr;  // (mean, rstd) per row of the last post-norm LayerNorm
 };
-constexpr int kWsRegions = 10;
+constexpr int kWsRegions = 11;
 // w2v2_forward splits a batch into up to kSplit row ranges that run
 // concurrently, one per stream (the caller's and kSplit - 1 of the model's).
 constexpr int kSplit = 2;
@@ -393,7 +396,7 @@ w2v2_status run_frontend(w2v2_model* m, const Ws& w, const float* pcm, const int
     if (c.feat_norm == W2V2_NORM_LAYER) {
       W2V2_LAUNCH(m, s, "conv_ln_gelu",
                   launch_layernorm(dt, nullptr, out, g.M, c.conv_dim[i], m->conv[i].gamma,
-                                   m->conv[i].beta, c.eps, nullptr, out, m->act, s));
+                                   m->conv[i].beta, c.eps, nullptr, out, m->act, nullptr, s));
     }
     cur = out;
     tin = m->T[i];
@@ -403,9 +406,15 @@ w2v2_status run_frontend(w2v2_model* m, const Ws& w, const float* pcm, const int
   return W2V2_OK;
 }
 
+// LayerNorm applied to a GEMM's residual as it is read (post-norm blocks)
+struct ResNorm {
+  const float2* stats;
+  const float *gamma, *beta;
+};
+
 w2v2_status gemm_linear(w2v2_model* m, hipStream_t s, const char* name, int role, const void* A, int M, int N,
                         int K, const void* W, const float* bias, int act, const float* residual, float* out32,
-                        void* outt, int64_t ldc) {
+                        void* outt, int64_t ldc, const ResNorm* rn = nullptr) {
   GemmArgs g;
   g.role = role;
   g.A = A;
@@ -419,6 +428,11 @@ w2v2_status gemm_linear(w2v2_model* m, hipStream_t s, const char* name, int role
   g.bias = bias;
   g.act = act;
   g.residual = residual;
+  if (rn) {
+    g.res_stats = rn->stats;
+    g.res_gamma = rn->gamma;
+    g.res_beta = rn->beta;
+  }
   g.out_f32 = out32;
   g.out_t = outt;
   g.ldc = ldc;
@@ -444,7 +458,7 @@ w2v2_status run_encoder(w2v2_model* m, const Ws& w, const void* feat, int B, flo
 
   // feature projection: LN over channels, then Linear C -> d (fp32 residual stream)
   W2V2_LAUNCH(m, s, "layernorm",
-              launch_layernorm(dt, nullptr, feat, M, cl, m->fp_g, m->fp_b, eps, nullptr, w.x, 0, s));
+              launch_layernorm(dt, nullptr, feat, M, cl, m->fp_g, m->fp_b, eps, nullptr, w.x, 0, nullptr, s));
   W2V2_TRY(gemm_linear(m, s, "gemm_feature_proj", kGemmProj, w.x, M, d, cl, m->fp_w, m->fp_bias, 0, nullptr, w.h, nullptr, d));
 
   // positional conv: h = z + GELU(posconv(z) + bias)
@@ -474,34 +488,45 @@ w2v2_status run_encoder(w2v2_model* m, const Ws& w, const void* feat, int B, flo
     g.c_group = Cg;
     W2V2_LAUNCH(m, s, "pos_conv_gemm", launch_gemm(dt, g, s));
   }
+  // Post-norm: every LayerNorm writes only the GEMM operand x and the row
+  // statistics; the raw residual sum stays in h, and the next residual GEMM
+  // (out-proj, FFN2) applies that LayerNorm to h as it reads it.
+  // Stable pre-norm: the LayerNorms feed x only and h is the plain sum.
   const bool stable = c.stable_layer_norm != 0;
+  ResNorm rn{w.lnst, m->enc_g, m->enc_b};
   if (!stable)
     W2V2_LAUNCH(m, s, "layernorm",
-                launch_layernorm(dt, w.h, nullptr, M, d, m->enc_g, m->enc_b, eps, w.h, w.x, 0, s));
+                launch_layernorm(dt, w.h, nullptr, M, d, m->enc_g, m->enc_b, eps, nullptr, w.x, 0, w.lnst, s));
 
   for (int l = 0; l < c.layers; ++l) {
     const w2v2_model::Layer& L = m->layers[l];
     if (stable)
       W2V2_LAUNCH(m, s, "layernorm",
-                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, nullptr, w.x, 0, s));
+                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, nullptr, w.x, 0, nullptr, s));
     W2V2_TRY(gemm_linear(m, s, "gemm_qkv", kGemmQKV, w.x, M, 3 * d, d, L.wqkv, L.bqkv, 0, nullptr, nullptr, w.qkv, 3 * d));
     W2V2_LAUNCH(m, s, "attention", launch_attention(dt, w.qkv, w.attn, B, T, rows, c.heads, d / c.heads, s));
-    W2V2_TRY(gemm_linear(m, s, "gemm_out_proj", kGemmOut, w.attn, M, d, d, L.wo, L.bo, 0, w.h, w.h, nullptr, d));
-    if (stable)
+    W2V2_TRY(gemm_linear(m, s, "gemm_out_proj", kGemmOut, w.attn, M, d, d, L.wo, L.bo, 0, w.h, w.h, nullptr, d,
+                         stable ? nullptr : &rn));
+    if (stable) {
       W2V2_LAUNCH(m, s, "layernorm",
-                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln2_g, L.ln2_b, eps, nullptr, w.x, 0, s));
-    else
+                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln2_g, L.ln2_b, eps, nullptr, w.x, 0, nullptr, s));
+    } else {
       W2V2_LAUNCH(m, s, "layernorm",
-                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, w.h, w.x, 0, s));
+                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, nullptr, w.x, 0, w.lnst, s));
+      rn = ResNorm{w.lnst, L.ln1_g, L.ln1_b};
+    }
     W2V2_TRY(gemm_linear(m, s, "gemm_ffn1", kGemmFFN1, w.x, M, F, d, L.w1, L.b1, m->act, nullptr, nullptr, w.ffn, F));
-    W2V2_TRY(gemm_linear(m, s, "gemm_ffn2", kGemmFFN2, w.ffn, M, d, F, L.w2, L.b2, 0, w.h, w.h, nullptr, d));
-    if (!stable)
+    W2V2_TRY(gemm_linear(m, s, "gemm_ffn2", kGemmFFN2, w.ffn, M, d, F, L.w2, L.b2, 0, w.h, w.h, nullptr, d,
+                         stable ? nullptr : &rn));
+    if (!stable) {
       W2V2_LAUNCH(m, s, "layernorm",
-                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln2_g, L.ln2_b, eps, w.h, w.x, 0, s));
+                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln2_g, L.ln2_b, eps, nullptr, w.x, 0, w.lnst, s));
+      rn = ResNorm{w.lnst, L.ln2_g, L.ln2_b};
+    }
   }
   if (stable)
     W2V2_LAUNCH(m, s, "layernorm",
-                launch_layernorm(dt, w.h, nullptr, M, d, m->enc_g, m->enc_b, eps, nullptr, w.x, 0, s));
+                launch_layernorm(dt, w.h, nullptr, M, d, m->enc_g, m->enc_b, eps, nullptr, w.x, 0, nullptr, s));
   if (!pk) {
     W2V2_TRY(gemm_linear(m, s, "gemm_ctc_head", kGemmHead, w.x, M, c.vocab, d, m->head_w, m->head_b, 0, nullptr,
                          logits, nullptr, c.vocab));
@@ -784,6 +809,7 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
       (size_t)M * d * ds,                                 // attn
       (size_t)M * F * ds,                                 // ffn
       (size_t)G * Bm * (m->Tf + K) * Cg * ds,             // zg
+      (size_t)M * 8,                                      // lnst
       (size_t)tl_i32_words(c) * 4 + (size_t)(c.n_conv + 1) * Bm * 8,   // true-length lengths/starts + bases
       (size_t)tl_rows_count(c, m->T, m->Tf) * 8,          // true-length row tables
   };
@@ -810,6 +836,7 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
   m->w.attn = wsb + offs[7];
   m->w.ffn = wsb + offs[8];
   m->w.zg = wsb + offs[9];
+  m->w.lnst = (float2*)(wsb + offs[10]);
   for (int i = 0; i < kWsRegions; ++i) m->row_bytes[i] = sizes[i] / (size_t)Bm;
   if (hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming) != hipSuccess) {
     m->ev_fork = nullptr;
@@ -828,9 +855,9 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
       return fail(W2V2_E_DEVICE, "hipEventCreate failed");
     }
   }
-  m->tl_i32 = (int32_t*)(wsb + offs[10]);
-  m->tl_base = (int64_t*)(wsb + offs[10] + (size_t)tl_i32_words(c) * 4);
-  m->tl_rows = (int64_t*)(wsb + offs[11]);
+  m->tl_i32 = (int32_t*)(wsb + offs[11]);
+  m->tl_base = (int64_t*)(wsb + offs[11] + (size_t)tl_i32_words(c) * 4);
+  m->tl_rows = (int64_t*)(wsb + offs[12]);
   // pinned staging of the true-length tables (lengths, starts, valid, bases)
   m->tl_bytes = (size_t)tl_i32_words(c) * 4 + (size_t)(c.n_conv + 1) * Bm * 8;
   if (hipHostMalloc((void**)&m->tl_pinned, m->tl_bytes, hipHostMallocDefault) != hipSuccess) {
@@ -890,6 +917,7 @@ Ws ws_rows(const w2v2_model* m, int b0) {
   r.attn = at(m->w.attn, 7);
   r.ffn = at(m->w.ffn, 8);
   r.zg = at(m->w.zg, 9);
+  r.lnst = (float2*)at(m->w.lnst, 10);
   return r;
 }
 

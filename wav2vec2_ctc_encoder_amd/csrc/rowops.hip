@@ -48,7 +48,7 @@ template <typename T, typename XT, int NV>
 __global__ __launch_bounds__(256) void layernorm_kernel(const XT* x, int64_t R, int C,
                                                         const float* __restrict__ gamma,
                                                         const float* __restrict__ beta, float eps,
-                                                        float* y32, T* yt, int act) {
+                                                        float* y32, T* yt, int act, float2* __restrict__ stats) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= R) return;
@@ -77,6 +77,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const XT* x, int64_t R, 
     }
   }
   const float rstd = rsqrtf(wave_sum(q) * invC + eps);
+  if (stats && lane == 0) stats[row] = make_float2(mean, rstd);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = 4 * (lane + 64 * i);
@@ -101,14 +102,14 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const XT* x, int64_t R, 
 
 template <typename T, typename XT>
 hipError_t ln_dispatch(const XT* x, int64_t R, int C, const float* g, const float* b, float eps, float* y32,
-                       T* yt, int act, hipStream_t s) {
+                       T* yt, int act, float2* st, hipStream_t s) {
   const dim3 grid((unsigned)((R + 3) / 4)), block(256);
   const int nv = (C + 255) / 256;
-  if (nv <= 1) hipLaunchKernelGGL((layernorm_kernel<T, XT, 1>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act);
-  else if (nv == 2) hipLaunchKernelGGL((layernorm_kernel<T, XT, 2>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act);
-  else if (nv == 3) hipLaunchKernelGGL((layernorm_kernel<T, XT, 3>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act);
-  else if (nv == 4) hipLaunchKernelGGL((layernorm_kernel<T, XT, 4>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act);
-  else hipLaunchKernelGGL((layernorm_kernel<T, XT, 8>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act);
+  if (nv <= 1) hipLaunchKernelGGL((layernorm_kernel<T, XT, 1>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act, st);
+  else if (nv == 2) hipLaunchKernelGGL((layernorm_kernel<T, XT, 2>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act, st);
+  else if (nv == 3) hipLaunchKernelGGL((layernorm_kernel<T, XT, 3>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act, st);
+  else if (nv == 4) hipLaunchKernelGGL((layernorm_kernel<T, XT, 4>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act, st);
+  else hipLaunchKernelGGL((layernorm_kernel<T, XT, 8>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act, st);
   return hipGetLastError();
 }
 
@@ -177,14 +178,15 @@ inline int grid_for(int64_t work) {
 
 hipError_t launch_layernorm(DType t, const float* x_f32, const void* x_t, int64_t R, int32_t C,
                             const float* gamma, const float* beta, float eps, float* y_f32, void* y_t,
-                            int32_t act, hipStream_t s) {
+                            int32_t act, float2* stats, hipStream_t s) {
   if (R <= 0) return hipSuccess;
   if (t == DType::F16) {
-    if (x_f32) return ln_dispatch<half_t, float>(x_f32, R, C, gamma, beta, eps, y_f32, (half_t*)y_t, act, s);
-    return ln_dispatch<half_t, half_t>((const half_t*)x_t, R, C, gamma, beta, eps, y_f32, (half_t*)y_t, act, s);
+    if (x_f32) return ln_dispatch<half_t, float>(x_f32, R, C, gamma, beta, eps, y_f32, (half_t*)y_t, act, stats, s);
+    return ln_dispatch<half_t, half_t>((const half_t*)x_t, R, C, gamma, beta, eps, y_f32, (half_t*)y_t, act, stats,
+                                       s);
   }
-  if (x_f32) return ln_dispatch<float, float>(x_f32, R, C, gamma, beta, eps, y_f32, (float*)y_t, act, s);
-  return ln_dispatch<float, float>((const float*)x_t, R, C, gamma, beta, eps, y_f32, (float*)y_t, act, s);
+  if (x_f32) return ln_dispatch<float, float>(x_f32, R, C, gamma, beta, eps, y_f32, (float*)y_t, act, stats, s);
+  return ln_dispatch<float, float>((const float*)x_t, R, C, gamma, beta, eps, y_f32, (float*)y_t, act, stats, s);
 }
 
 hipError_t launch_pos_pack(DType t, const float* h, int32_t B, int32_t T, RowSpan rows, int32_t d, int32_t G,

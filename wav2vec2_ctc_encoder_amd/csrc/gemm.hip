@@ -17,14 +17,15 @@
 //
 // gemm_dlds_kernel (fp16, K % 64 == 0, N > 32; the hot path): block tile
 //   128x128 or 128x64, waves 2 x 2, v_mfma_f32_32x32x16_f16.  K advances in
-//   64-wide steps through a two-stage LDS ring filled by wave-wide direct
+//   64-wide steps through two LDS buffers filled by wave-wide direct
 //   global->LDS loads (global_load_lds_dwordx4, 16 bytes per lane) into
-//   XOR-swizzled 128-byte rows; explicit vmcnt waits, one barrier per step,
-//   fragments double-buffered in registers with MFMAs and LDS reads
-//   interleaved.  Epilogue: bias and activation in registers, then each wave
-//   stages its 32-row slabs row-major in LDS and writes whole rows (residual
-//   add, fp32 and/or fp16 stores), because the 32x32 accumulator layout
-//   would otherwise scatter 16-byte pieces over 32 rows per store.
+//   XOR-swizzled 128-byte rows; explicit vmcnt waits, one barrier per step.
+//   All MFMA fragments of the next step are read from LDS into registers
+//   while the current step's MFMAs run, so no MFMA waits on an LDS read.
+//   Epilogue: bias and activation in registers, then each wave stages its
+//   32-row slabs row-major in LDS and writes whole rows (residual add, fp32
+//   and/or fp16 stores), because the 32x32 accumulator layout would
+//   otherwise scatter 16-byte pieces over 32 rows per store.
 //
 // gemm_kernel (fp32 mode and the remaining shapes): block tile BM x BN, K
 //   step of 128 bytes per row (64 fp16 / 32 fp32), double-buffered LDS with
@@ -185,7 +186,10 @@ __device__ inline bool epilogue_staged_ok(const GemmArgs& a) {
 // with LPR consecutive lanes covering one row, so the residual loads and the
 // output stores move whole contiguous rows.  LDS operations of one wave run in
 // order, so no barrier is needed between the write and the read-back.
-template <int TM, int TN, int ACT>
+// NT: non-temporal output stores (conv outputs: hundreds of MB written once
+// and read once by the next layer; keeping them out of the caches leaves the
+// L2 to the operand tiles).
+template <int TM, int TN, int ACT, bool NT>
 __device__ inline void epilogue_staged(const GemmArgs& a, f16x (&acc)[TN][TM], float* stage, int m_base,
                                        int n_base, int group) {
   constexpr int W = TN * 32;    // columns of the wave block
@@ -227,13 +231,20 @@ __device__ inline void epilogue_staged(const GemmArgs& a, f16x (&acc)[TN][TM], f
           x1.x += r1.x; x1.y += r1.y; x1.z += r1.z; x1.w += r1.w;
         }
         if (a.out_f32) {
-          *(float4*)(a.out_f32 + off) = x0;
-          *(float4*)(a.out_f32 + off + 4) = x1;
+          const f4 v0 = {x0.x, x0.y, x0.z, x0.w}, v1 = {x1.x, x1.y, x1.z, x1.w};
+          if constexpr (NT) {
+            __builtin_nontemporal_store(v0, (f4*)(a.out_f32 + off));
+            __builtin_nontemporal_store(v1, (f4*)(a.out_f32 + off + 4));
+          } else {
+            *(f4*)(a.out_f32 + off) = v0;
+            *(f4*)(a.out_f32 + off + 4) = v1;
+          }
         }
         if (a.out_t) {
           const h8v hv = {(half_t)x0.x, (half_t)x0.y, (half_t)x0.z, (half_t)x0.w,
                           (half_t)x1.x, (half_t)x1.y, (half_t)x1.z, (half_t)x1.w};
-          *(h8v*)((half_t*)a.out_t + off) = hv;
+          if constexpr (NT) __builtin_nontemporal_store(hv, (h8v*)((half_t*)a.out_t + off));
+          else *(h8v*)((half_t*)a.out_t + off) = hv;
         }
       }
     }
@@ -389,48 +400,36 @@ __device__ inline void dma16(const void* gptr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
 }
 
-// s_waitcnt vmcnt(LPS * ahead) for a run-time ahead in [0, MAXA]; the count
-// is an instruction immediate, so each case is its own instruction.
-// Encoding (gfx9): vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8];
-// expcnt / lgkmcnt are left at their maxima (no wait).
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left at their maxima (no wait).
+// Encoding (gfx9): vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 template <int N>
 __device__ inline void wait_vmcnt_imm() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
-template <int LPS, int MAXA>
-__device__ inline void wait_vmcnt_steps(int ahead) {
-  if constexpr (MAXA >= 3) {
-    if (ahead >= 3) { wait_vmcnt_imm<LPS * 3>(); return; }
-  }
-  if constexpr (MAXA >= 2) {
-    if (ahead == 2) { wait_vmcnt_imm<LPS * 2>(); return; }
-  }
-  if constexpr (MAXA >= 1) {
-    if (ahead == 1) { wait_vmcnt_imm<LPS>(); return; }
-  }
-  wait_vmcnt_imm<0>();
-}
+// s_waitcnt lgkmcnt(0): every LDS read of this wave has returned.
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8)); }
 
-template <int BM, int BN, int WM, int WN, int STAGES, int BKB, int ROLE, int SCHED = 0>
-__global__ __launch_bounds__(256, 1) void gemm_dlds_kernel(GemmArgs a) {
-  constexpr int TM = BM / WM / 32;
-  constexpr int TN = BN / WN / 32;
-  constexpr int CPR = BKB / 16;          // 16-byte chunks per tile row (8 or 4)
-  constexpr int RPI = 64 / CPR;          // tile rows per 1 KB wave load
-  constexpr int KEYDIV = 16 / CPR;       // rows sharing a bank-group phase
-  constexpr int KS = BKB / 32;           // 16-wide K slices per step
-  constexpr int JA = BM / RPI / 4;       // 1 KB load instructions per wave per stage (A)
-  constexpr int JB = BN / RPI / 4;       // (B)
-  constexpr int LPS = JA + JB;           // loads per thread per stage
-  static_assert(WM * WN == 4 && TM >= 1 && TN >= 1, "4 waves");
-  static_assert(JA >= 1 && JB >= 1 && LPS * (STAGES - 2) <= 63 && STAGES <= 5, "tile / vmcnt range");
+// WPE: waves per SIMD the register budget is fitted to (2 for 128x128 tiles,
+// 3 for 128x64, which LDS also allows: 64 / 48 KB per workgroup).
+template <int BM, int BN, int ROLE, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemm_dlds_kernel(GemmArgs a) {
+  constexpr int WM = 2, WN = 2;
+  constexpr int TM = BM / WM / 32;  // 32x32 blocks per wave along m
+  constexpr int TN = BN / WN / 32;  // ... along n
+  constexpr int CPR = 8;            // 16-byte chunks per tile row: 64 fp16 of K per step
+  constexpr int RPI = 64 / CPR;     // tile rows per 1 KB wave load
+  constexpr int KEYDIV = 16 / CPR;  // rows sharing a bank-group phase
+  constexpr int KS = 4;             // 16-wide K slices per step
+  constexpr int JA = BM / RPI / 4;  // 1 KB load instructions per wave per step (A)
+  constexpr int JB = BN / RPI / 4;  // (B)
+  constexpr int LPS = JA + JB;      // loads per thread per step
+  constexpr int ABUF = BM * CPR, BBUF = BN * CPR;  // uint4 per buffer
+  static_assert(TM >= 1 && TN >= 1 && JA >= 1 && JB >= 1 && LPS <= 63, "tile");
 
-  // one array for both operands so that the epilogue can reuse all of it
-  __shared__ uint4 smem[STAGES * (BM + BN) * CPR];
-  uint4 (*sA)[BM * CPR] = reinterpret_cast<uint4 (*)[BM * CPR]>(smem);
-  uint4 (*sB)[BN * CPR] = reinterpret_cast<uint4 (*)[BN * CPR]>(smem + STAGES * BM * CPR);
-  static_assert(4 * 32 * (TN * 32 + 4) * 4 <= STAGES * (BM + BN) * CPR * 16, "epilogue staging fits");
+  // [A buffer 0][A buffer 1][B buffer 0][B buffer 1]; the epilogue reuses all of it
+  __shared__ uint4 smem[2 * (ABUF + BBUF)];
+  static_assert(4 * 32 * (TN * 32 + 4) * 4 <= 2 * (ABUF + BBUF) * 16, "epilogue staging fits");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -452,15 +451,15 @@ __global__ __launch_bounds__(256, 1) void gemm_dlds_kernel(GemmArgs a) {
   const char* Abase = (const char*)a.A + (int64_t)group * a.a_group * 2;
   const char* Bbase = (const char*)a.B + (int64_t)group * a.b_group * 2;
 
-  // source rows (clamped) with the swizzled chunk folded in
+  // source rows (clamped) with the swizzled chunk folded in: LDS chunk p of
+  // tile row r holds source chunk p ^ key(r)
   const int pos = lane & (CPR - 1);
   const char* asrc[JA];
 #pragma unroll
   for (int j = 0; j < JA; ++j) {
     const int r = (wave * JA + j) * RPI + lane / CPR;
     const int m = min(m0 + r, a.M - 1);
-    asrc[j] = Abase + a_row_offset(a, m) * 2 +
-              ((pos ^ ((r / KEYDIV) & (CPR - 1))) << 4);
+    asrc[j] = Abase + a_row_offset(a, m) * 2 + ((pos ^ ((r / KEYDIV) & (CPR - 1))) << 4);
   }
   const char* bsrc[JB];
 #pragma unroll
@@ -469,19 +468,36 @@ __global__ __launch_bounds__(256, 1) void gemm_dlds_kernel(GemmArgs a) {
     const int n = min(n0 + r, a.N - 1);
     bsrc[j] = Bbase + (int64_t)n * a.K * 2 + ((pos ^ ((r / KEYDIV) & (CPR - 1))) << 4);
   }
-
-  const uint32_t ldsA = (uint32_t)(uintptr_t)&sA[0][0], ldsB = (uint32_t)(uintptr_t)&sB[0][0];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&smem[0];
   auto issue = [&](int kt, int buf) {
-    const int64_t koff = (int64_t)kt * BKB;
+    const int64_t koff = (int64_t)kt * 128;
 #pragma unroll
     for (int j = 0; j < JA; ++j)
       dma16(asrc[j] + koff,
-            __builtin_amdgcn_readfirstlane(ldsA + (uint32_t)((buf * BM * CPR + (wave * JA + j) * 64) * 16)));
+            __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((buf * ABUF + (wave * JA + j) * 64) * 16)));
 #pragma unroll
     for (int j = 0; j < JB; ++j)
       dma16(bsrc[j] + koff,
-            __builtin_amdgcn_readfirstlane(ldsB + (uint32_t)((buf * BN * CPR + (wave * JB + j) * 64) * 16)));
+            __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((2 * ABUF + buf * BBUF + (wave * JB + j) * 64) * 16)));
   };
+
+  // per-lane LDS offsets (uint4 units, buffer 0) of every fragment of a step:
+  // 32x32x16 operand lane l holds row l % 32, k chunk 2 * slice + l / 32
+  const int l32 = lane & 31, lg = lane >> 5;
+  int aoff[KS][TM], boff[KS][TN];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int R = wm * TM * 32 + j * 32 + l32;
+      aoff[ks][j] = R * CPR + ((ks * 2 + lg) ^ ((R / KEYDIV) & (CPR - 1)));
+    }
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int R = wn * TN * 32 + i * 32 + l32;
+      boff[ks][i] = 2 * ABUF + R * CPR + ((ks * 2 + lg) ^ ((R / KEYDIV) & (CPR - 1)));
+    }
+  }
 
   f16x acc[TN][TM];
 #pragma unroll
@@ -491,81 +507,75 @@ __global__ __launch_bounds__(256, 1) void gemm_dlds_kernel(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = a.K / (BKB / 2);
-#pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
-    if (st < nk) issue(st, st);
-
-  const int l32 = lane & 31, lg = lane >> 5;
-  // per-lane LDS row offsets (uint4 units) and swizzle keys of the fragment rows
-  int arow[TM], akey[TM], brow[TN], bkey[TN];
-#pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const int R = wm * TM * 32 + j * 32 + l32;
-    arow[j] = R * CPR;
-    akey[j] = (R / KEYDIV) & (CPR - 1);
-  }
-#pragma unroll
-  for (int i = 0; i < TN; ++i) {
-    const int R = wn * TN * 32 + i * 32 + l32;
-    brow[i] = R * CPR;
-    bkey[i] = (R / KEYDIV) & (CPR - 1);
-  }
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // wait for this step's loads while the later steps already issued
-    // (min(STAGES - 2, nk - 1 - kt) of them, LPS loads each) stay in flight;
-    // vector-memory loads retire in order, so vmcnt(n) leaves the newest n
-    // outstanding.  Then publish the step to the whole workgroup.
-    const int ahead = min(STAGES - 2, nk - 1 - kt);
-    wait_vmcnt_steps<LPS, STAGES - 2>(ahead);
-    __builtin_amdgcn_s_barrier();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-    const int buf = kt % STAGES;
-    const uint4* A_ = sA[buf];
-    const uint4* B_ = sB[buf];
-    uint4 wv[2][TN], av[2][TM];
-#pragma unroll
-    for (int i = 0; i < TN; ++i) wv[0][i] = B_[brow[i] + ((0 * 2 + lg) ^ bkey[i])];
-#pragma unroll
-    for (int j = 0; j < TM; ++j) av[0][j] = A_[arow[j] + ((0 * 2 + lg) ^ akey[j])];
+  // two register sets of a whole step's fragments, alternating by step parity
+  uint4 fa0[KS][TM], fb0[KS][TN], fa1[KS][TM], fb1[KS][TN];
+  auto read_frags = [&](int buf, uint4 (&fa)[KS][TM], uint4 (&fb)[KS][TN]) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < KS) {
 #pragma unroll
-        for (int i = 0; i < TN; ++i) wv[cur ^ 1][i] = B_[brow[i] + (((ks + 1) * 2 + lg) ^ bkey[i])];
+      for (int i = 0; i < TN; ++i) fb[ks][i] = smem[boff[ks][i] + buf * BBUF];
 #pragma unroll
-        for (int j = 0; j < TM; ++j) av[cur ^ 1][j] = A_[arow[j] + (((ks + 1) * 2 + lg) ^ akey[j])];
-      }
+      for (int j = 0; j < TM; ++j) fa[ks][j] = smem[aoff[ks][j] + buf * ABUF];
+    }
+  };
+  const int nk = a.K / 64;
+  // Step kt: the fragments of kt are in (fac, fbc) and buffer kt & 1 is no
+  // longer read by this wave.  Wait for this wave's loads of step kt + 1 (the
+  // only ones in flight); after the barrier every wave's have landed and
+  // every wave holds its step-kt fragments, so buffer kt & 1 may be refilled
+  // with step kt + 2 while the MFMAs of kt run interleaved with the reads of
+  // kt + 1.  That read is unconditional (one basic block for the scheduler):
+  // past the last step it reads a stale, in-bounds buffer and is never used.
+  auto step = [&](int kt, int bcur, uint4 (&fac)[KS][TM], uint4 (&fbc)[KS][TN], uint4 (&fan)[KS][TM],
+                  uint4 (&fbn)[KS][TN]) {
+    wait_vmcnt_imm<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + 2 < nk) issue(kt + 2, bcur);
+    read_frags(bcur ^ 1, fan, fbn);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
         for (int j = 0; j < TM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, wv[cur][i]),
-                                                             __builtin_bit_cast(h8, av[cur][j]), acc[i][j], 0, 0, 0);
-    }
-    if constexpr (SCHED == 1) {
-      // interleave: one MFMA, then the LDS fragment reads that fit under it
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, fbc[ks][i]),
+                                                             __builtin_bit_cast(h8, fac[ks][j]), acc[i][j], 0, 0, 0);
+    // one MFMA, one LDS read, alternately; the remaining MFMAs after
 #pragma unroll
-      for (int i = 0; i < TM * TN * KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
+    for (int q = 0; q < KS * (TM + TN); ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    // all LDS reads of this buffer have been consumed by the MFMAs above;
-    // make sure they completed before the next barrier lets the buffer refill
-    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
-  }
+    __builtin_amdgcn_sched_group_barrier(0x008, KS * TM * TN - KS * (TM + TN), 0);
+    wait_lgkm0();
+  };
 
+  issue(0, 0);
+  if (nk > 1) {
+    issue(1, 1);
+    wait_vmcnt_imm<LPS>();
+  } else {
+    wait_vmcnt_imm<0>();
+  }
+  __builtin_amdgcn_s_barrier();
+  read_frags(0, fa0, fb0);
+  wait_lgkm0();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, 0, fa0, fb0, fa1, fb1);
+    step(kt + 1, 1, fa1, fb1, fa0, fb0);
+  }
+  if (kt < nk) step(kt, 0, fa0, fb0, fa1, fb1);
+
+  constexpr bool NT = ROLE == kGemmConv;
   if (epilogue_staged_ok(a)) {
-    // every wave is done reading the stages before any overwrites them
+    // every wave is done reading the buffers before any overwrites them
     __builtin_amdgcn_s_barrier();
     float* stage = reinterpret_cast<float*>(smem) + wave * 32 * (TN * 32 + 4);
     const int m_base = m0 + wm * TM * 32, n_base = n0 + wn * TN * 32;
-    if (a.act == 1) epilogue_staged<TM, TN, 1>(a, acc, stage, m_base, n_base, group);
-    else if (a.act == 2) epilogue_staged<TM, TN, 2>(a, acc, stage, m_base, n_base, group);
-    else epilogue_staged<TM, TN, 0>(a, acc, stage, m_base, n_base, group);
+    if (a.act == 1) epilogue_staged<TM, TN, 1, NT>(a, acc, stage, m_base, n_base, group);
+    else if (a.act == 2) epilogue_staged<TM, TN, 2, NT>(a, acc, stage, m_base, n_base, group);
+    else epilogue_staged<TM, TN, 0, NT>(a, acc, stage, m_base, n_base, group);
     return;
   }
   const bool vec = epilogue_vec_ok(a);
@@ -603,11 +613,10 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int ST, int BKB, int ROLE>
+template <int BM, int BN, int ROLE, int WPE>
 hipError_t launch_dlds(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_dlds_kernel<BM, BN, 2, 2, ST, BKB, ROLE, 1>), dim3(tiles, 1, a.groups), dim3(256), 0, s,
-                     a);
+  hipLaunchKernelGGL((gemm_dlds_kernel<BM, BN, ROLE, WPE>), dim3(tiles, 1, a.groups), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -622,8 +631,8 @@ hipError_t launch_shape(const GemmArgs& a, hipStream_t s) {
       // linears: out-proj, FFN2, projection) 128x64 tiles balance the CUs
       // better.  The threshold was measured with the two batch halves of a
       // forward running concurrently (half-batch FFN1 / QKV: M = 3196).
-      if (a.N > 64 && (a.N <= 512 || tiles128 >= 400)) return launch_dlds<128, 128, 2, 128, ROLE>(a, s);
-      return launch_dlds<128, 64, 2, 128, ROLE>(a, s);
+      if (a.N > 64 && (a.N <= 512 || tiles128 >= 400)) return launch_dlds<128, 128, ROLE, 2>(a, s);
+      return launch_dlds<128, 64, ROLE, 3>(a, s);
     }
   }
   if (a.N <= 32) return launch_t<T, 128, 32, 4, 1, ROLE>(a, s);

@@ -63,6 +63,26 @@ __device__ inline void store8<float>(float* dst, const float* v) {
   *(float4*)(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// Copy n samples of one PCM row, starting at sample base, into LDS; samples
+// at or past vl read as zero.  Each thread issues its loads in groups of 8
+// before storing any of them, so their latencies overlap instead of adding
+// up (a load-store loop waits for every load before the next one issues).
+__device__ inline void stage_pcm(float* xs, const float* __restrict__ row, int64_t base, int n, int vl) {
+  for (int i0 = 0; i0 < n; i0 += 256 * 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 256 + (int)threadIdx.x;
+      v[u] = (i < n && base + i < vl) ? row[base + i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 256 + (int)threadIdx.x;
+      if (i < n) xs[i] = v[u];
+    }
+  }
+}
+
 // KT: compile-time tap count (taps >= k carry zero weights).
 template <typename T, int KT>
 __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pcm, const int32_t* __restrict__ valid,
@@ -86,6 +106,7 @@ __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pc
   int vl = valid[b];
   vl = vl < 0 ? 0 : (vl > L ? L : vl);
   const int64_t base = (int64_t)t0 * stride;
+  // a few samples per thread: a plain loop (batched loads measured slower here)
   for (int i = threadIdx.x; i < nsamp; i += 256) {
     const int64_t idx = base + i;
     xs[i] = (idx < vl) ? pcm[(int64_t)b * L + idx] : 0.f;
@@ -194,10 +215,7 @@ __global__ __launch_bounds__(256) void gn0_stats_kernel(const float* __restrict_
   int vl = valid[b];
   vl = vl < 0 ? 0 : (vl > L ? L : vl);
   const int64_t base = (int64_t)t0 * stride;
-  for (int i = threadIdx.x; i < nsamp; i += 256) {
-    const int64_t idx = base + i;
-    xs[i] = (idx < vl) ? pcm[(int64_t)b * L + idx] : 0.f;
-  }
+  stage_pcm(xs, pcm + (int64_t)b * L, base, nsamp, vl);
   __syncthreads();
   const int ns = k + k * (k + 1) / 2;
   double* out = part + ((int64_t)b * gridDim.x + chunk) * ns;
@@ -254,7 +272,7 @@ __global__ __launch_bounds__(256) void gn0_stats_kernel(const float* __restrict_
 __global__ __launch_bounds__(256) void gn0_merge_kernel(const double* __restrict__ part, int nchunk, int k, int T0,
                                                          const int32_t* __restrict__ rows_len,
                                                          double* __restrict__ merged) {
-  constexpr int kBatch = 16;
+  constexpr int kBatch = 32;
   __shared__ double stage[kBatch * 152];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int Tb = rows_len ? rows_len[b] : T0;
@@ -275,7 +293,20 @@ __global__ __launch_bounds__(256) void gn0_merge_kernel(const double* __restrict
   for (int c0 = 0; c0 < nuse; c0 += kBatch) {
     const int nb = min(kBatch, nuse - c0);
     __syncthreads();
-    for (int i = tid; i < nb * ns; i += 256) stage[i] = src[(int64_t)c0 * ns + i];
+    // all loads of the batch issue before any store (their latencies overlap)
+    for (int i0 = 0; i0 < nb * ns; i0 += 256 * 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 256 + tid;
+        v[u] = i < nb * ns ? src[(int64_t)c0 * ns + i] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 256 + tid;
+        if (i < nb * ns) stage[i] = v[u];
+      }
+    }
     __syncthreads();
     for (int c = 0; c < nb; ++c) {
       const double* pc = stage + c * ns;

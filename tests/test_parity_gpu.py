@@ -319,10 +319,13 @@ def test_full_workload_fp32(name):
     _check_ids(cfg, logits, vf, ids, lens)
 
 
-def test_base_rand_affine_fp16():
-    """Every norm gain/shift, bias and weight-norm gain random at base size."""
-    cfg = synth.BASE_10S_B1.replace(rand_affine=True, window=64000, weight_seed=99)
-    _say("base 4 s rand_affine fp16")
+@pytest.mark.parametrize("conv_bias", [False, True])
+def test_base_rand_affine_fp16(conv_bias):
+    """Every norm gain/shift, bias and weight-norm gain random at base size
+    (512 feature channels: the matrix-core conv0 of the group-norm layout,
+    with and without a conv bias folded into the GroupNorm shift)."""
+    cfg = synth.BASE_10S_B1.replace(rand_affine=True, window=64000, weight_seed=99, conv_bias=conv_bias)
+    _say(f"base 4 s rand_affine fp16 conv_bias={conv_bias}")
     ref, vf_ref = _oracle(cfg, (0,))
     logits, vf, ids, lens = _gpu_forward(cfg, precision="fp16")
     _gate_fp16(logits, ref, vf_ref)

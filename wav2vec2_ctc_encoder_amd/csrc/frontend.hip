@@ -194,6 +194,103 @@ __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pc
   else frames(ActTag<1>{});
 }
 
+// conv0 + GroupNorm + GELU of the fp16 mode with the convolution on fp32
+// matrix cores.  For a block of 32 frames and 32 channels the conv is a
+// 32x32 product with K = taps: D[c][f] = sum_j w[c][j] x[stride f + j],
+// v_mfma_f32_32x32x2_f32 taking 2 taps per instruction (fp32 products and
+// sums, as on the vector path; taps 2 KS > k carry zero weights).  A lane
+// then holds frame f = l % 32 and channels 8q + 4 (l / 32) + 0..3 of the
+// block; it applies the folded GroupNorm scale / shift and the GELU, packs
+// fp16 and writes the values to its wave's LDS slab, from which whole
+// 128-byte row pieces (64 channels of a frame) go to memory.  This takes the
+// ten multiply-adds per output off the vector unit, which bounds the
+// vector-path kernel.
+template <int KS, int ACT>
+__global__ __launch_bounds__(256) void conv0_mfma_kernel(const float* __restrict__ pcm,
+                                                         const int32_t* __restrict__ valid, int L,
+                                                         const float* __restrict__ w0,
+                                                         const float* __restrict__ bias, int C, int k, int stride,
+                                                         int T0, RowSpan rows, half_t* __restrict__ y,
+                                                         const float2* __restrict__ ss) {
+  typedef float f16v __attribute__((ext_vector_type(16)));
+  typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+  constexpr int KT = 2 * KS;   // padded taps
+  constexpr int SP = 72;       // slab row pitch in halves: 64 channels + 16 B
+  extern __shared__ float smem[];
+  float* wl = smem;                                    // [C][KT]
+  float2* ssl = reinterpret_cast<float2*>(wl + C * KT);  // [C] (scale, shift with the conv bias folded in)
+  float* xs = reinterpret_cast<float*>(ssl + C);         // [(kChunk - 1) * stride + KT]
+  const int nx = (kChunk - 1) * stride + KT;
+  half_t* slab = reinterpret_cast<half_t*>(xs + ((nx + 3) & ~3));  // [4][32][SP]
+
+  const int b = blockIdx.y;
+  const int t0 = blockIdx.x * kChunk;
+  const int Tb = rows.len ? rows.len[b] : T0;  // frames of this row
+  const int nf = min(kChunk, Tb - t0);
+  if (nf <= 0) return;
+  const int64_t ybase = rows.start ? (int64_t)rows.start[b] : (int64_t)b * T0;  // its first output row
+
+  int vl = valid[b];
+  vl = vl < 0 ? 0 : (vl > L ? L : vl);
+  // samples of every frame slot of the chunk (frames past nf are computed
+  // from whatever samples are there and never stored); zero at or past vl
+  const int64_t base = (int64_t)t0 * stride;
+  for (int i = threadIdx.x; i < nx; i += 256) {
+    const int64_t idx = base + i;
+    xs[i] = (idx < vl) ? pcm[(int64_t)b * L + idx] : 0.f;
+  }
+  for (int i = threadIdx.x; i < C * KT; i += 256) {
+    const int c = i / KT, j = i - c * KT;
+    wl[i] = j < k ? w0[c * k + j] : 0.f;
+  }
+  for (int c = threadIdx.x; c < C; c += 256) {
+    const float2 p = ss[(int64_t)b * C + c];
+    ssl[c] = make_float2(p.x, bias ? fmaf(bias[c], p.x, p.y) : p.y);
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, lg = lane >> 5;
+  half_t* st = slab + wave * 32 * SP;
+  for (int fb = wave * 32; fb < nf; fb += 128) {
+    float xb[KS];
+#pragma unroll
+    for (int q = 0; q < KS; ++q) xb[q] = xs[stride * (fb + l32) + 2 * q + lg];
+    for (int cg = 0; cg < C; cg += 64) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int cb = cg + 32 * h;
+        f16v acc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int q = 0; q < KS; ++q)
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wl[(cb + l32) * KT + 2 * q + lg], xb[q], acc, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int cl = 32 * h + 8 * q + 4 * lg;  // first of this lane's 4 channels within the 64
+          h4v o;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float2 p = ssl[cg + cl + i];
+            o[i] = (half_t)act_fn<ACT>(fmaf(acc[4 * q + i], p.x, p.y));
+          }
+          *(h4v*)(st + l32 * SP + cl) = o;
+        }
+      }
+      // the slab holds 32 frames x 64 channels; LDS operations of one wave
+      // complete in order, so the read-back sees every lane's writes
+#pragma unroll
+      for (int ps = 0; ps < 4; ++ps) {
+        const int r = ps * 8 + (lane >> 3), col = (lane & 7) * 8;
+        const uint4 v = *(const uint4*)(st + r * SP + col);
+        const int f = fb + r;
+        if (f < nf) *(uint4*)(y + (ybase + t0 + f) * C + cg + col) = v;
+      }
+    }
+  }
+}
+
 // Per (row, chunk of kStatChunk frames): means of the k shifted sequences and
 // their co-moments (upper triangle, row-major i <= j), in fp64.
 // Output layout per chunk: [mu_0 .. mu_{k-1}, S_00, S_01, .., S_{k-1,k-1}].
@@ -397,6 +494,22 @@ hipError_t conv0_k(int k, const float* pcm, const int32_t* valid, int32_t L, int
                    const float* bias, int32_t C, int32_t stride, int32_t T0, RowSpan rows, void* y,
                    const float2* ss, const float* gamma, const float* beta, float eps, int32_t act,
                    hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    // GroupNorm layout, 9 or 10 taps, whole 64-channel slabs: matrix-core conv
+    if (!gamma && (k == 9 || k == 10) && C % 64 == 0 && C <= 512) {
+      constexpr int KS = 5;
+      const int nchunk = (T0 + kChunk - 1) / kChunk;
+      const int nx = (kChunk - 1) * stride + 2 * KS;
+      const size_t lds = (size_t)C * 2 * KS * 4 + (size_t)C * 8 + (size_t)((nx + 3) & ~3) * 4 + 4 * 32 * 72 * 2;
+      if (act == 2)
+        hipLaunchKernelGGL((conv0_mfma_kernel<KS, 2>), dim3(nchunk, B), dim3(256), lds, s, pcm, valid, L, w0, bias,
+                           C, k, stride, T0, rows, (half_t*)y, ss);
+      else
+        hipLaunchKernelGGL((conv0_mfma_kernel<KS, 1>), dim3(nchunk, B), dim3(256), lds, s, pcm, valid, L, w0, bias,
+                           C, k, stride, T0, rows, (half_t*)y, ss);
+      return hipGetLastError();
+    }
+  }
   if (k == 10)
     return conv0_t<T, 10>(pcm, valid, L, B, w0, bias, C, k, stride, T0, rows, y, ss, gamma, beta, eps, act, s);
   return conv0_t<T, 16>(pcm, valid, L, B, w0, bias, C, k, stride, T0, rows, y, ss, gamma, beta, eps, act, s);

@@ -192,44 +192,81 @@ __device__ inline bool epilogue_staged_ok(const GemmArgs& a) {
 template <int TM, int TN, int ACT, bool NT>
 __device__ inline void epilogue_staged(const GemmArgs& a, f16x (&acc)[TN][TM], float* stage, int m_base,
                                        int n_base, int group) {
-  constexpr int W = TN * 32;    // columns of the wave block
-  constexpr int P = W + 4;      // padded row pitch (floats)
-  constexpr int LPR = W / 8;    // lanes per row in the read-back
-  constexpr int RPP = 64 / LPR; // rows per read-back pass
+  constexpr int W = TN * 32;     // columns of the wave block
+  constexpr int P = W + 4;       // padded row pitch (floats)
+  constexpr int LPR = W / 8;     // lanes per row in the read-back
+  constexpr int RPP = 64 / LPR;  // rows per read-back pass
+  constexpr int NPS = 32 / RPP;  // read-back passes per 32-row slab
   const int lane = threadIdx.x & 63, l32 = lane & 31, lg = lane >> 5;
   const float* bias = a.bias ? a.bias + (int64_t)group * a.bias_group : nullptr;
   const int64_t cg = (int64_t)group * a.c_group;
   const int rrow = lane / LPR, rcol = (lane % LPR) * 8;
+  // Operands that do not depend on the row are loaded once, and every load
+  // goes to a clamped in-bounds address without a branch, so the loads issue
+  // together instead of each waiting behind the math of the previous chunk
+  // (N % 8 == 0 here; values of clamped columns or rows are never stored).
+  float4 bv[TN][4];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      bv[i][q] = bias ? *(const float4*)(bias + min(n_base + i * 32 + 8 * q + 4 * lg, a.N - 4))
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  const int nr = min(n_base + rcol, a.N - 8);  // the lane's 8 read-back columns
+  float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0, e0 = g0, e1 = g0;
+  if (a.res_stats) {
+    g0 = *(const float4*)(a.res_gamma + nr);
+    g1 = *(const float4*)(a.res_gamma + nr + 4);
+    e0 = *(const float4*)(a.res_beta + nr);
+    e1 = *(const float4*)(a.res_beta + nr + 4);
+  }
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
+    // this slab's residual rows, requested before its activation math
+    float4 r0[NPS], r1[NPS];
+    float2 rs[NPS];
+    if (a.residual) {
+#pragma unroll
+      for (int ps = 0; ps < NPS; ++ps) {
+        const int m = min(m_base + j * 32 + ps * RPP + rrow, a.M - 1);
+        const float* r = a.residual + cg + c_row_offset(a, m) + nr;
+        r0[ps] = *(const float4*)r;
+        r1[ps] = *(const float4*)(r + 4);
+        rs[ps] = a.res_stats ? a.res_stats[m] : make_float2(0.f, 1.f);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int nl = i * 32 + 8 * q + 4 * lg;
-        const int n = n_base + nl;
-        float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-        if (bias && n < a.N) {
-          const float4 bb = *(const float4*)(bias + n);
-          v.x += bb.x; v.y += bb.y; v.z += bb.z; v.w += bb.w;
-        }
+        float4 v = make_float4(acc[i][j][4 * q] + bv[i][q].x, acc[i][j][4 * q + 1] + bv[i][q].y,
+                               acc[i][j][4 * q + 2] + bv[i][q].z, acc[i][j][4 * q + 3] + bv[i][q].w);
         v.x = act_fn<ACT>(v.x); v.y = act_fn<ACT>(v.y); v.z = act_fn<ACT>(v.z); v.w = act_fn<ACT>(v.w);
         *(float4*)(stage + l32 * P + nl) = v;
       }
     }
 #pragma unroll
-    for (int ps = 0; ps < 32 / RPP; ++ps) {
+    for (int ps = 0; ps < NPS; ++ps) {
       const int row = ps * RPP + rrow;
       const int m = m_base + j * 32 + row, n = n_base + rcol;
       float4 x0 = *(const float4*)(stage + row * P + rcol);
       float4 x1 = *(const float4*)(stage + row * P + rcol + 4);
+      if (a.residual) {
+        float4 u0 = r0[ps], u1 = r1[ps];
+        if (a.res_stats) {
+          // the residual's LayerNorm: (r - mean) * rstd * gamma + beta
+          const float mu = rs[ps].x, rstd = rs[ps].y;
+          u0.x = (u0.x - mu) * rstd * g0.x + e0.x; u0.y = (u0.y - mu) * rstd * g0.y + e0.y;
+          u0.z = (u0.z - mu) * rstd * g0.z + e0.z; u0.w = (u0.w - mu) * rstd * g0.w + e0.w;
+          u1.x = (u1.x - mu) * rstd * g1.x + e1.x; u1.y = (u1.y - mu) * rstd * g1.y + e1.y;
+          u1.z = (u1.z - mu) * rstd * g1.z + e1.z; u1.w = (u1.w - mu) * rstd * g1.w + e1.w;
+        }
+        x0.x += u0.x; x0.y += u0.y; x0.z += u0.z; x0.w += u0.w;
+        x1.x += u1.x; x1.y += u1.y; x1.z += u1.z; x1.w += u1.w;
+      }
       if (m < a.M && n < a.N) {
         const int64_t off = cg + c_row_offset(a, m) + n;
-        if (a.residual) {
-          const float4 r0 = residual4(a, m, n, a.residual + off), r1 = residual4(a, m, n + 4, a.residual + off + 4);
-          x0.x += r0.x; x0.y += r0.y; x0.z += r0.z; x0.w += r0.w;
-          x1.x += r1.x; x1.y += r1.y; x1.z += r1.z; x1.w += r1.w;
-        }
         if (a.out_f32) {
           const f4 v0 = {x0.x, x0.y, x0.z, x0.w}, v1 = {x1.x, x1.y, x1.z, x1.w};
           if constexpr (NT) {

@@ -53,6 +53,17 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const XT* x, int64_t R, 
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= R) return;
   const XT* xr = x + row * C;
+  // the affine parameters are requested with the row, not after the
+  // reductions, so their latency overlaps the row's
+  float4 gv[NV], bv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = 4 * (lane + 64 * i);
+    if (c < C) {
+      gv[i] = *(const float4*)(gamma + c);
+      bv[i] = *(const float4*)(beta + c);
+    }
+  }
   float4 v[NV];
   float s = 0.f;
 #pragma unroll
@@ -82,8 +93,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const XT* x, int64_t R, 
   for (int i = 0; i < NV; ++i) {
     const int c = 4 * (lane + 64 * i);
     if (c < C) {
-      const float4 g = *(const float4*)(gamma + c);
-      const float4 b = *(const float4*)(beta + c);
+      const float4 g = gv[i], b = bv[i];
       float4 o;
       o.x = (v[i].x - mean) * rstd * g.x + b.x;
       o.y = (v[i].y - mean) * rstd * g.y + b.y;

@@ -205,6 +205,8 @@ __global__ __launch_bounds__(256) void conv0_kernel(const float* __restrict__ pc
 // 128-byte row pieces (64 channels of a frame) go to memory.  This takes the
 // ten multiply-adds per output off the vector unit, which bounds the
 // vector-path kernel.
+constexpr int kConv0MaxC = 512;  // channels the matrix-core conv0 handles (its LDS budget)
+
 template <int KS, int ACT>
 __global__ __launch_bounds__(256) void conv0_mfma_kernel(const float* __restrict__ pcm,
                                                          const int32_t* __restrict__ valid, int L,
@@ -232,20 +234,37 @@ __global__ __launch_bounds__(256) void conv0_mfma_kernel(const float* __restrict
 
   int vl = valid[b];
   vl = vl < 0 ? 0 : (vl > L ? L : vl);
-  // samples of every frame slot of the chunk (frames past nf are computed
-  // from whatever samples are there and never stored); zero at or past vl
-  const int64_t base = (int64_t)t0 * stride;
-  for (int i = threadIdx.x; i < nx; i += 256) {
-    const int64_t idx = base + i;
-    xs[i] = (idx < vl) ? pcm[(int64_t)b * L + idx] : 0.f;
-  }
-  for (int i = threadIdx.x; i < C * KT; i += 256) {
-    const int c = i / KT, j = i - c * KT;
-    wl[i] = j < k ? w0[c * k + j] : 0.f;
-  }
-  for (int c = threadIdx.x; c < C; c += 256) {
-    const float2 p = ss[(int64_t)b * C + c];
-    ssl[c] = make_float2(p.x, bias ? fmaf(bias[c], p.x, p.y) : p.y);
+  // Weights, scale / shift and samples go to LDS with every thread's loads
+  // issued before its stores, so their latencies overlap.  Samples cover
+  // every frame slot of the chunk (frames past nf are computed from whatever
+  // samples are there and never stored) and read zero at or past vl.
+  {
+    constexpr int NWL = (kConv0MaxC * KT + 255) / 256, NSS = (kConv0MaxC + 255) / 256;
+    float wr[NWL];
+    float2 sr[NSS];
+    float br[NSS];
+#pragma unroll
+    for (int u = 0; u < NWL; ++u) {
+      const int i = (int)threadIdx.x + 256 * u, c = i / KT, j = i - c * KT;
+      wr[u] = (i < C * KT && j < k) ? w0[c * k + j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < NSS; ++u) {
+      const int c = (int)threadIdx.x + 256 * u;
+      sr[u] = c < C ? ss[(int64_t)b * C + c] : make_float2(0.f, 0.f);
+      br[u] = (c < C && bias) ? bias[c] : 0.f;
+    }
+    stage_pcm(xs, pcm + (int64_t)b * L, (int64_t)t0 * stride, nx, vl);
+#pragma unroll
+    for (int u = 0; u < NWL; ++u) {
+      const int i = (int)threadIdx.x + 256 * u;
+      if (i < C * KT) wl[i] = wr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NSS; ++u) {
+      const int c = (int)threadIdx.x + 256 * u;
+      if (c < C) ssl[c] = make_float2(sr[u].x, fmaf(br[u], sr[u].x, sr[u].y));
+    }
   }
   __syncthreads();
 
@@ -496,7 +515,7 @@ hipError_t conv0_k(int k, const float* pcm, const int32_t* valid, int32_t L, int
                    hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     // GroupNorm layout, 9 or 10 taps, whole 64-channel slabs: matrix-core conv
-    if (!gamma && (k == 9 || k == 10) && C % 64 == 0 && C <= 512) {
+    if (!gamma && (k == 9 || k == 10) && C % 64 == 0 && C <= kConv0MaxC) {
       constexpr int KS = 5;
       const int nchunk = (T0 + kChunk - 1) / kChunk;
       const int nx = (kChunk - 1) * stride + 2 * KS;

@@ -663,12 +663,14 @@ hipError_t launch_shape(const GemmArgs& a, hipStream_t s) {
     // direct-to-LDS pipeline: whole 64-wide K steps, N wide enough to fill a tile
     if (a.K % 64 == 0 && a.N > 32) {
       const int64_t tiles128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.groups;
-      // 128x128 tiles read less per MFMA and win on the 512-wide conv GEMMs
-      // and wherever there are at least ~400 of them; with fewer (N = 768
-      // linears: out-proj, FFN2, projection) 128x64 tiles balance the CUs
-      // better.  The threshold was measured with the two batch halves of a
-      // forward running concurrently (half-batch FFN1 / QKV: M = 3196).
-      if (a.N > 64 && (a.N <= 512 || tiles128 >= 400)) return launch_dlds<128, 128, ROLE, 2>(a, s);
+      // 128x128 tiles read less per MFMA and win on the 512-wide conv GEMMs,
+      // wherever there are at least ~400 of them, and on long-K products
+      // (FFN2, K = 3072) from ~150 of them; with fewer (N = 768 linears with
+      // short K: out-proj, projection) 128x64 tiles balance the CUs better.
+      // The thresholds were measured with the two batch halves of a forward
+      // running concurrently (half-batch FFN1 / QKV / FFN2: M = 3196).
+      if (a.N > 64 && (a.N <= 512 || tiles128 >= 400 || (a.K >= 2048 && tiles128 >= 150)))
+        return launch_dlds<128, 128, ROLE, 2>(a, s);
       return launch_dlds<128, 64, ROLE, 3>(a, s);
     }
   }

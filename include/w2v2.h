@@ -238,6 +238,10 @@ w2v2_status w2v2_forward(w2v2_model* model, const float* pcm, const int32_t* val
  * Asynchronous on `stream` like w2v2_forward: the lengths are copied into a
  * pinned staging buffer that w2v2_create allocated and uploaded on that
  * stream; a call first waits for the previous call's upload from that buffer.
+ * As in w2v2_forward, for batch >= 2 the two halves of the rows run
+ * concurrently (each packed on its own), the second on the model's stream
+ * forked after the upload and joined back; profiling every kernel runs one
+ * pass.  Results are bit-identical to one pass.
  * Allocates nothing.  Calls that share a model must not overlap.
  * Errors: W2V2_E_ARG (null model/pcm/valid_host/logits, batch out of range,
  * a valid[b] outside [0, window]), W2V2_E_DEVICE (copy or launch failure).

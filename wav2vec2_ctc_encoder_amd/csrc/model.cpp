@@ -971,6 +971,51 @@ w2v2_status w2v2_forward(w2v2_model* m, const float* pcm, const int32_t* valid, 
   return W2V2_OK;
 }
 
+// One row range [b0, b0 + nb) of a true-length call on stream s: its packing
+// (device spans and starts relative to the range's own packed rows, already
+// uploaded), its row tables in the range's share of each table region, then
+// the frontend and encoder on the range's workspace slice.
+w2v2_status true_length_rows(w2v2_model* m, const float* pcm, int b0, int nb, const int64_t* P, float* logits,
+                             hipStream_t s) {
+  const w2v2_config& c = m->cfg;
+  const int n = c.n_conv, Bm = c.max_batch;
+  const int32_t* dlen = m->tl_i32;
+  const int32_t* dstart = m->tl_i32 + (size_t)n * Bm;
+  const int32_t* dvalid = m->tl_i32 + (size_t)2 * n * Bm;
+  Packing pk;
+  for (int i = 0; i < n; ++i) {
+    pk.P[i] = P[i];
+    pk.lvl[i].len = dlen + (size_t)i * Bm + b0;
+    pk.lvl[i].start = dstart + (size_t)i * Bm + b0;
+  }
+  const int Tf = m->Tf, Cg = c.hidden / c.pos_groups;
+  RowTable tabs[kMaxRowTables];
+  int nt = 0, tmax = 1;
+  int64_t off = 0;  // each table region holds Bm * frames entries; this range uses rows b0 .. b0 + nb of it
+  for (int i = 1; i < n; ++i) {
+    tabs[nt] = RowTable{pk.lvl[i].start, pk.lvl[i].len, m->tl_base + (size_t)(i - 1) * Bm + b0,
+                        (int64_t)c.conv_stride[i] * c.conv_dim[i - 1], m->tl_rows + off + (int64_t)b0 * m->T[i]};
+    pk.a_rows[i] = tabs[nt].out;
+    off += (int64_t)Bm * m->T[i];
+    tmax = std::max(tmax, m->T[i]);
+    ++nt;
+  }
+  tabs[nt] = RowTable{pk.lvl[n - 1].start, pk.lvl[n - 1].len, m->tl_base + (size_t)(n - 1) * Bm + b0, Cg,
+                      m->tl_rows + off + (int64_t)b0 * Tf};
+  pk.pos_rows = tabs[nt++].out;
+  off += (int64_t)Bm * Tf;
+  tabs[nt] = RowTable{pk.lvl[n - 1].start, pk.lvl[n - 1].len, m->tl_base + (size_t)n * Bm + b0, c.vocab,
+                      m->tl_rows + off + (int64_t)b0 * Tf};
+  pk.head_rows = tabs[nt++].out;
+  tmax = std::max(tmax, Tf);
+  W2V2_LAUNCH(m, s, "row_tables", launch_row_tables(tabs, nt, nb, tmax, s));
+
+  const Ws w = ws_rows(m, b0);
+  const void* feat = nullptr;
+  W2V2_TRY(run_frontend(m, w, pcm + (size_t)b0 * c.window, dvalid + b0, nb, s, &feat, &pk));
+  return run_encoder(m, w, feat, nb, logits + (size_t)b0 * Tf * c.vocab, s, &pk);
+}
+
 w2v2_status w2v2_forward_true_length(w2v2_model* m, const float* pcm, const int32_t* valid_host, int32_t batch,
                                      float* logits, int32_t* vframes, void* stream) {
   W2V2_TRY(check_forward_args(m, pcm, valid_host, batch, logits));
@@ -982,6 +1027,15 @@ w2v2_status w2v2_forward_true_length(w2v2_model* m, const float* pcm, const int3
   DeviceGuard guard(m->device);
   hipStream_t s = (hipStream_t)stream;
 
+  // Like w2v2_forward, the rows are cut into near-equal ranges that run
+  // concurrently (profiling every kernel: one range).  Each range is packed
+  // on its own: its rows' frames are consecutive from the start of its
+  // workspace slice.
+  const bool serial = B == 1 || (m->prof_on && m->prof_only.empty());
+  const int np = serial ? 1 : std::min(B, kSplit);
+  int r0[kSplit + 1] = {};
+  for (int p = 0; p < np; ++p) r0[p + 1] = r0[p] + B / np + (p < B % np ? 1 : 0);
+
   // host: frames and packed starts of every row at every conv level, staged
   // in pinned memory; the previous call's upload from it must have finished
   const int64_t words = tl_i32_words(c);
@@ -991,10 +1045,10 @@ w2v2_status w2v2_forward_true_length(w2v2_model* m, const float* pcm, const int3
   int64_t* blob = m->tl_pinned;
   std::memset(blob, 0, m->tl_bytes);
   int32_t* len = (int32_t*)blob;                     // [n][Bm]
-  int32_t* start = len + (size_t)n * Bm;             // [n][Bm]
+  int32_t* start = len + (size_t)n * Bm;             // [n][Bm], relative to the row's range
   int32_t* vcopy = start + (size_t)n * Bm;           // [Bm]
   int64_t* base = blob + words / 2;                  // [n + 1][Bm]
-  Packing pk;
+  int64_t P[kSplit][W2V2_MAX_CONV] = {};
   for (int b = 0; b < B; ++b) {
     vcopy[b] = valid_host[b];
     int64_t f = valid_host[b];
@@ -1003,64 +1057,52 @@ w2v2_status w2v2_forward_true_length(w2v2_model* m, const float* pcm, const int3
       len[(size_t)i * Bm + b] = (int32_t)f;
     }
   }
-  for (int i = 0; i < n; ++i) {
-    int64_t acc = 0;
-    for (int b = 0; b < B; ++b) {
-      start[(size_t)i * Bm + b] = (int32_t)acc;
-      acc += len[(size_t)i * Bm + b];
+  for (int p = 0; p < np; ++p)
+    for (int i = 0; i < n; ++i) {
+      int64_t acc = 0;
+      for (int b = r0[p]; b < r0[p + 1]; ++b) {
+        start[(size_t)i * Bm + b] = (int32_t)acc;
+        acc += len[(size_t)i * Bm + b];
+      }
+      P[p][i] = acc;
     }
-    pk.P[i] = acc;
-  }
   // table bases: conv i reads row b's input window at packed input row
   // start_{i-1}[b] + t * stride_i; the positional conv reads row b's padded
   // segment of T + K frames; the head writes row b's frame t at (b * T + t) * V
+  // (row b counted from the first row of its range)
   const int Tf = m->Tf, K = c.pos_kernel, Cg = c.hidden / c.pos_groups;
-  for (int i = 1; i < n; ++i)
-    for (int b = 0; b < B; ++b)
-      base[(size_t)(i - 1) * Bm + b] = (int64_t)start[(size_t)(i - 1) * Bm + b] * c.conv_dim[i - 1];
-  for (int b = 0; b < B; ++b) {
-    base[(size_t)(n - 1) * Bm + b] = (int64_t)b * (Tf + K) * Cg;
-    base[(size_t)n * Bm + b] = (int64_t)b * Tf * c.vocab;
-  }
+  for (int p = 0; p < np; ++p)
+    for (int b = r0[p]; b < r0[p + 1]; ++b) {
+      for (int i = 1; i < n; ++i)
+        base[(size_t)(i - 1) * Bm + b] = (int64_t)start[(size_t)(i - 1) * Bm + b] * c.conv_dim[i - 1];
+      base[(size_t)(n - 1) * Bm + b] = (int64_t)(b - r0[p]) * (Tf + K) * Cg;
+      base[(size_t)n * Bm + b] = (int64_t)(b - r0[p]) * Tf * c.vocab;
+    }
   if (hipMemcpyAsync(m->tl_i32, blob, m->tl_bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
       hipEventRecord(m->tl_copied, s) != hipSuccess)
     return fail(W2V2_E_DEVICE, "upload of the row lengths failed");
   m->tl_pending = true;
 
-  const int32_t* dlen = m->tl_i32;
-  const int32_t* dstart = m->tl_i32 + (size_t)n * Bm;
-  const int32_t* dvalid = m->tl_i32 + (size_t)2 * n * Bm;
-  for (int i = 0; i < n; ++i) {
-    pk.lvl[i].len = dlen + (size_t)i * Bm;
-    pk.lvl[i].start = dstart + (size_t)i * Bm;
+  if (np == 1) {
+    W2V2_TRY(true_length_rows(m, pcm, 0, B, P[0], logits, s));
+  } else {
+    // the fork follows the upload, so every range sees the tables
+    if (hipEventRecord(m->ev_fork, s) != hipSuccess) return fail(W2V2_E_DEVICE, "fork of the streams failed");
+    for (int p = 1; p < np; ++p)
+      if (hipStreamWaitEvent(m->aux[p], m->ev_fork, 0) != hipSuccess)
+        return fail(W2V2_E_DEVICE, "fork of the streams failed");
+    w2v2_status st = W2V2_OK;
+    for (int p = 0; p < np && st == W2V2_OK; ++p)
+      st = true_length_rows(m, pcm, r0[p], r0[p + 1] - r0[p], P[p], logits, p == 0 ? s : m->aux[p]);
+    for (int p = 1; p < np; ++p)
+      if (hipEventRecord(m->ev_join[p], m->aux[p]) != hipSuccess || hipStreamWaitEvent(s, m->ev_join[p], 0) != hipSuccess)
+        return fail(W2V2_E_DEVICE, "join of the streams failed");
+    if (st != W2V2_OK) return st;
   }
-  RowTable tabs[kMaxRowTables];
-  int nt = 0, tmax = 1;
-  int64_t off = 0;
-  for (int i = 1; i < n; ++i) {
-    tabs[nt] = RowTable{pk.lvl[i].start, pk.lvl[i].len, m->tl_base + (size_t)(i - 1) * Bm,
-                        (int64_t)c.conv_stride[i] * c.conv_dim[i - 1], m->tl_rows + off};
-    pk.a_rows[i] = m->tl_rows + off;
-    off += (int64_t)Bm * m->T[i];
-    tmax = std::max(tmax, m->T[i]);
-    ++nt;
-  }
-  tabs[nt++] = RowTable{pk.lvl[n - 1].start, pk.lvl[n - 1].len, m->tl_base + (size_t)(n - 1) * Bm, Cg,
-                        m->tl_rows + off};
-  pk.pos_rows = m->tl_rows + off;
-  off += (int64_t)Bm * Tf;
-  tabs[nt++] = RowTable{pk.lvl[n - 1].start, pk.lvl[n - 1].len, m->tl_base + (size_t)n * Bm, c.vocab,
-                        m->tl_rows + off};
-  pk.head_rows = m->tl_rows + off;
-  tmax = std::max(tmax, Tf);
-  W2V2_LAUNCH(m, s, "row_tables", launch_row_tables(tabs, nt, B, tmax, s));
-
-  const void* feat = nullptr;
-  W2V2_TRY(run_frontend(m, m->w, pcm, dvalid, B, s, &feat, &pk));
-  W2V2_TRY(run_encoder(m, m->w, feat, B, logits, s, &pk));
   if (vframes)
     W2V2_LAUNCH(m, s, "valid_frames",
-                launch_valid_frames(dvalid, B, c.window, c.n_conv, c.conv_kernel, c.conv_stride, vframes, s));
+                launch_valid_frames(m->tl_i32 + (size_t)2 * n * Bm, B, c.window, c.n_conv, c.conv_kernel,
+                                    c.conv_stride, vframes, s));
   return W2V2_OK;
 }
 

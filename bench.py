@@ -124,10 +124,15 @@ def read_traffic(kernel: str, key: str = "traffic_bytes_per_launch") -> float | 
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "wav2vec2_ctc_encoder_amd", "csrc", kv.get("source", ""))
-    if not os.path.exists(src):
-        return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    # the kernel's sources: every file listed (the GEMM and the header whose
+    # device functions it inlines), hashed in order
+    h = hashlib.sha256()
+    for name in kv.get("source", "").split():
+        src = os.path.join(ROOT, "wav2vec2_ctc_encoder_amd", "csrc", name)
+        if not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    sha = h.hexdigest()[:16]
     if sha != kv.get("source_sha16"):
         return None
     try:

@@ -16,31 +16,35 @@ inline size_t dsize(DType t) { return t == DType::F16 ? 2 : 4; }
 
 // Exact (erf) GELU, x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), with erf from
 // Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26
-// (Hastings' rational approximation, |error| <= 1.5e-7 for x >= 0):
-//   erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
-//   t = 1 / (1 + p z).
-// With e = poly(t) exp(-z^2) and z = |x| / sqrt 2, GELU(x) = x - x e / 2 for
-// x >= 0 and x e / 2 for x < 0.  Absolute error <= ~2e-7 |x| in fp32, far
-// below the fp16 operand rounding the fp16 mode adds; GELU(0) is exactly 0.
+// (Hastings' rational approximation, |error| <= 1.5e-7 for z >= 0):
+//   erfc(z) = (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
+//   t = 1 / (1 + p z),  z = |x| / sqrt 2.
+// With q = erfc(z) / 2, GELU(x) = x - |x| q for x >= 0 and -|x| q for x < 0,
+// i.e. max(x, 0) - |x| q: one fused multiply-add after q, no select.  The
+// halving is folded into the coefficients and 1/sqrt 2 into p; the exponent
+// -z^2 log2(e) is -(x k)^2 with k^2 = log2(e) / 2.  Absolute error <= ~3e-7
+// |x| in fp32, far below the fp16 operand rounding the fp16 mode adds;
+// GELU(0) is exactly 0.
 __device__ inline float gelu_erf(float x) {
-  const float z = fabsf(x) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-  float p = fmaf(1.061405429f, t, -1.453152027f);
-  p = fmaf(p, t, 1.421413741f);
-  p = fmaf(p, t, -0.284496736f);
-  p = fmaf(p, t, 0.254829592f);
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.23164189f, ax, 1.0f));  // p / sqrt 2 = 0.3275911 / sqrt 2
+  float p = fmaf(0.5307027145f, t, -0.7265760135f);                    // a5 / 2, a4 / 2
+  p = fmaf(p, t, 0.7107068705f);                                        // a3 / 2
+  p = fmaf(p, t, -0.142248368f);                                        // a2 / 2
+  p = fmaf(p, t, 0.127414796f);                                         // a1 / 2
   p *= t;
-  const float e = p * __builtin_amdgcn_exp2f(-(z * z) * 1.4426950408889634f);
-  const float h = 0.5f * x * e;
-  return x >= 0.f ? x - h : h;
+  const float u = x * 0.84932180028801904f;                             // k = sqrt(log2(e) / 2)
+  const float q = p * __builtin_amdgcn_exp2f(-(u * u));
+  return fmaf(-ax, q, fmaxf(x, 0.f));
 }
 
 // tanh approximation of GELU, x/2 (1 + tanh(u)) with u = sqrt(2/pi)(x +
 // 0.044715 x^3) (Hendrycks & Gimpel), written as x * sigmoid(2u) =
-// x / (1 + exp(-2u)): saturates cleanly to x and to -0 for large |x|.
+// x / (1 + exp(-2u)): saturates cleanly to x and to -0 for large |x|.  The
+// two constant factors of the exponent, sqrt(2/pi) and -2 log2(e), are one.
 __device__ inline float gelu_tanh(float x) {
-  const float u = 0.7978845608028654f * fmaf(0.044715f * x, x * x, x);
-  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.8853900817779268f * u));  // 2 log2(e) u
+  const float v = fmaf(0.044715f * x, x * x, x);
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.3022081981443f * v));  // -2 log2(e) sqrt(2/pi)
 }
 
 // Activation codes of the kernels: 0 none, 1 erf GELU, 2 tanh GELU.  Hot

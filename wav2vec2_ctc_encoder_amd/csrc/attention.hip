@@ -247,6 +247,9 @@ __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restric
     for (int c = 0; c < NCH; ++c) qf[c] = *(const uint4*)(base + (int64_t)q * ld + c * 32 + lg * 8);
   }
 
+  // Keys past the row's last frame are read from that last frame (clamped,
+  // no branch): their scores are masked to -inf, so their probabilities are
+  // exactly 0 and their (finite) V rows add nothing.
   uint4 rk[KPT];
   uint2 rv[VPT][4];
   auto fetch = [&](int k0) {
@@ -254,8 +257,8 @@ __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restric
     for (int i = 0; i < KPT; ++i) {
       const int idx = tid + NT * i;
       if (idx < KCH) {
-        const int key = k0 + idx / (DH / 8), ch = idx % (DH / 8);
-        rk[i] = key < Tn ? *(const uint4*)(base + (int64_t)key * ld + dm + ch * 8) : make_uint4(0, 0, 0, 0);
+        const int key = min(k0 + idx / (DH / 8), Tn - 1), ch = idx % (DH / 8);
+        rk[i] = *(const uint4*)(base + (int64_t)key * ld + dm + ch * 8);
       }
     }
 #pragma unroll
@@ -265,8 +268,8 @@ __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restric
         const int dg = idx % (DH / 4), kg = idx / (DH / 4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = k0 + kg * 4 + r;
-          rv[i][r] = key < Tn ? *(const uint2*)(base + (int64_t)key * ld + 2 * dm + dg * 4) : make_uint2(0, 0);
+          const int key = min(k0 + kg * 4 + r, Tn - 1);
+          rv[i][r] = *(const uint2*)(base + (int64_t)key * ld + 2 * dm + dg * 4);
         }
       }
     }

@@ -113,7 +113,9 @@ def test_tiny_fp16_true_length_gates():
     _check_ids(cfg, logits, vf, ids, lens)
 
 
-@pytest.mark.parametrize("name,rows", [("base_16s_b8", (0, 5)), ("large_16s_b4", (1, 2))])
+# base_16s_b32: rows 0 and 31 are the first row of the first half and the
+# last row of the second half of the concurrent split
+@pytest.mark.parametrize("name,rows", [("base_16s_b8", (0, 5)), ("large_16s_b4", (1, 2)), ("base_16s_b32", (0, 31))])
 def test_full_workload_true_length_fp16_sampled_rows(name, rows):
     cfg = synth.PRESETS[name]
     if name == "large_16s_b4":
@@ -151,6 +153,9 @@ def test_row_bits_do_not_depend_on_the_batch():
     perm = np.array([5, 2, 7, 0, 1, 6, 3, 4])
     shuf, _, _, _ = _gpu_true_length(cfg, pcm[perm], valid[perm])
     assert np.array_equal(shuf, whole[perm])
+    # an odd sub-batch: halves of 3 and 2 rows
+    odd, _, _, _ = _gpu_true_length(cfg, pcm[1:6], valid[1:6], max_batch=8)
+    assert np.array_equal(odd, whole[1:6])
 
 
 def test_full_rows_equal_padded_mode_bitwise():

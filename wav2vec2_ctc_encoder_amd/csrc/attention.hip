@@ -134,8 +134,8 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
         if (key >= Tn) s[kb][r] = -INFINITY;
         mt = fmaxf(mt, s[kb][r]);
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = max_xor16(mt);
+    mt = max_xor32(mt);
     const float mnew = fmaxf(mrun, mt);
     const float alpha = exp2f((mrun - mnew) * c1);
     const float mc = mnew * c1;
@@ -182,8 +182,8 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
     }
   }
 
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
+  lsum = add_xor16(lsum);
+  lsum = add_xor32(lsum);
   const float inv = 1.f / lsum;
   const int q = q0 + lr;
   if (q < Tn) {
@@ -336,8 +336,8 @@ __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restric
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sc[kb][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mt = max_xor16(mt);
+      mt = max_xor32(mt);
       const float mnew = fmaxf(mrun, mt);
       const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * c1);
       const float mc = mnew * c1;
@@ -374,8 +374,8 @@ __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restric
   }
 
   if (!wave_live) return;
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
+  lsum = add_xor16(lsum);
+  lsum = add_xor32(lsum);
   const float inv = 1.f / lsum;
   const int q = qw + lr;
   if (q < Tn) {
@@ -389,10 +389,17 @@ __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restric
   }
 }
 
+// shared: another part of the batch runs concurrently.  The kernel then asks
+// for enough (unused) dynamic LDS that at most two of its workgroups share a
+// CU, which leaves room for a GEMM workgroup (64 KB) of the other part; with
+// the GPU to itself it takes up to three per CU.
 template <int DH, int NW>
-hipError_t launch_a16(const void* qkv, void* out, int B, int Tn, RowSpan rows, int H, hipStream_t s) {
+hipError_t launch_a16(const void* qkv, void* out, int B, int Tn, RowSpan rows, int H, bool shared, hipStream_t s) {
   const float c1 = 1.4426950408889634f / sqrtf((float)DH);
-  hipLaunchKernelGGL((attn16_kernel<DH, NW>), dim3((Tn + NW * 16 - 1) / (NW * 16), H, B), dim3(NW * 64), 0, s,
+  constexpr size_t kStatic = 2 * 64 * (DH / 8 + 1) * 16 + 2 * DH * (64 + 4) * 2;  // sK + sV
+  constexpr size_t kTwoPerCu = 56 * 1024;
+  const size_t pad = (shared && kStatic < kTwoPerCu) ? kTwoPerCu - kStatic : 0;
+  hipLaunchKernelGGL((attn16_kernel<DH, NW>), dim3((Tn + NW * 16 - 1) / (NW * 16), H, B), dim3(NW * 64), pad, s,
                      (const half_t*)qkv, (half_t*)out, Tn, rows, H, c1);
   return hipGetLastError();
 }
@@ -421,12 +428,12 @@ hipError_t launch_dh(const void* qkv, void* out, int B, int Tn, RowSpan rows, in
 bool attention_supported(int dh) { return dh == 16 || dh == 32 || dh == 64 || dh == 128; }
 
 hipError_t launch_attention(DType t, const void* qkv, void* out, int32_t B, int32_t T, RowSpan rows, int32_t H,
-                            int32_t dh, hipStream_t s) {
+                            int32_t dh, bool shared, hipStream_t s) {
   if (B <= 0 || T <= 0) return hipSuccess;
   // fp16: 16 queries per wave, 8 waves share each K/V tile
-  if (t == DType::F16 && dh == 32) return launch_a16<32, 8>(qkv, out, B, T, rows, H, s);
-  if (t == DType::F16 && dh == 64) return launch_a16<64, 8>(qkv, out, B, T, rows, H, s);
-  if (t == DType::F16 && dh == 128) return launch_a16<128, 8>(qkv, out, B, T, rows, H, s);
+  if (t == DType::F16 && dh == 32) return launch_a16<32, 8>(qkv, out, B, T, rows, H, shared, s);
+  if (t == DType::F16 && dh == 64) return launch_a16<64, 8>(qkv, out, B, T, rows, H, shared, s);
+  if (t == DType::F16 && dh == 128) return launch_a16<128, 8>(qkv, out, B, T, rows, H, shared, s);
   return t == DType::F16 ? launch_dh<half_t>(qkv, out, B, T, rows, H, dh, s)
                          : launch_dh<float>(qkv, out, B, T, rows, H, dh, s);
 }

@@ -47,6 +47,43 @@ __device__ inline float gelu_tanh(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.3022081981443f * v));  // -2 log2(e) sqrt(2/pi)
 }
 
+// Cross-lane reductions without the LDS crossbar.  v_permlane16_swap /
+// v_permlane32_swap (gfx950) with both operands x return, for every lane,
+// x of the lane and x of lane ^ 16 (lane ^ 32) as an (even row, odd row) /
+// (lower half, upper half) pair; combining the two with a commutative op
+// gives both lanes of a pair the same bits.
+__device__ inline float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float add_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// x + x of the lane `R` places away by rotation within its row of 16 (DPP
+// row_ror); for R = 8, 4, 2, 1 in turn every lane of a row pairs with a lane
+// holding the same partial sums, so the row ends with one value.
+template <int R>
+__device__ inline float add_ror(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + R, 0xF, 0xF, false));
+}
+// Sum over the 64 lanes of a wave, the same bits in every lane.
+__device__ inline float wave_sum64(float v) {
+  v = add_ror<8>(v);
+  v = add_ror<4>(v);
+  v = add_ror<2>(v);
+  v = add_ror<1>(v);
+  return add_xor32(add_xor16(v));
+}
+
 // Activation codes of the kernels: 0 none, 1 erf GELU, 2 tanh GELU.  Hot
 // loops take the code as a template argument (selected once per launch) so
 // that only one form is compiled into them.
@@ -191,9 +228,11 @@ hipError_t launch_valid_frames(const int32_t* valid, int32_t B, int32_t window, 
 // ----------------------------------------------------------------------------
 // With rows set, row b has its own rows.len[b] frames starting at packed row
 // rows.start[b] of qkv and out, and attends over those frames only.
+// shared: another part of the batch runs concurrently on the GPU (the fp16
+// kernel then leaves room on each CU for that part's GEMM workgroups).
 bool attention_supported(int dh);
 hipError_t launch_attention(DType t, const void* qkv, void* out, int32_t B, int32_t T, RowSpan rows,
-                            int32_t H, int32_t dh, hipStream_t s);
+                            int32_t H, int32_t dh, bool shared, hipStream_t s);
 
 // ----------------------------------------------------------------------------
 // CTC

@@ -40,11 +40,7 @@ struct ActTag {
   static constexpr int value = N;
 };
 
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
+__device__ inline float wave_sum(float v) { return wave_sum64(v); }
 
 template <typename T>
 __device__ inline void store8(T* dst, const float* v);

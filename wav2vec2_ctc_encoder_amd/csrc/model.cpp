@@ -220,6 +220,7 @@ struct Ws {
   float* h = nullptr;
   void *x = nullptr, *qkv = nullptr, *attn = nullptr, *ffn = nullptr, *zg = nullptr;
   float2* lnst = nullptr;  // (mean, rstd) per row of the last post-norm LayerNorm
+  bool shared = false;     // another part of the batch runs concurrently
 };
 constexpr int kWsRegions = 11;
 // w2v2_forward splits a batch into up to kSplit row ranges that run
@@ -504,7 +505,7 @@ w2v2_status run_encoder(w2v2_model* m, const Ws& w, const void* feat, int B, flo
       W2V2_LAUNCH(m, s, "layernorm",
                   launch_layernorm(dt, w.h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, nullptr, w.x, 0, nullptr, s));
     W2V2_TRY(gemm_linear(m, s, "gemm_qkv", kGemmQKV, w.x, M, 3 * d, d, L.wqkv, L.bqkv, 0, nullptr, nullptr, w.qkv, 3 * d));
-    W2V2_LAUNCH(m, s, "attention", launch_attention(dt, w.qkv, w.attn, B, T, rows, c.heads, d / c.heads, s));
+    W2V2_LAUNCH(m, s, "attention", launch_attention(dt, w.qkv, w.attn, B, T, rows, c.heads, d / c.heads, w.shared, s));
     W2V2_TRY(gemm_linear(m, s, "gemm_out_proj", kGemmOut, w.attn, M, d, d, L.wo, L.bo, 0, w.h, w.h, nullptr, d,
                          stable ? nullptr : &rn));
     if (stable) {
@@ -923,8 +924,9 @@ Ws ws_rows(const w2v2_model* m, int b0) {
 
 // Whole network on rows [b0, b0 + n) of the batch, on stream s.
 w2v2_status forward_rows(w2v2_model* m, const float* pcm, const int32_t* valid, int b0, int n, float* logits,
-                         hipStream_t s) {
-  const Ws w = ws_rows(m, b0);
+                         hipStream_t s, bool shared = false) {
+  Ws w = ws_rows(m, b0);
+  w.shared = shared;
   const void* feat = nullptr;
   W2V2_TRY(run_frontend(m, w, pcm + (size_t)b0 * m->cfg.window, valid + b0, n, s, &feat));
   return run_encoder(m, w, feat, n, logits + (size_t)b0 * m->Tf * m->cfg.vocab, s);
@@ -955,7 +957,7 @@ w2v2_status w2v2_forward(w2v2_model* m, const float* pcm, const int32_t* valid, 
     int b0 = 0;
     for (int p = 0; p < np && st == W2V2_OK; ++p) {
       const int n = batch / np + (p < batch % np ? 1 : 0);
-      st = forward_rows(m, pcm, valid, b0, n, logits, p == 0 ? s : m->aux[p]);
+      st = forward_rows(m, pcm, valid, b0, n, logits, p == 0 ? s : m->aux[p], np > 1);
       b0 += n;
     }
     // the caller's stream waits for every part whatever happened
@@ -976,7 +978,7 @@ w2v2_status w2v2_forward(w2v2_model* m, const float* pcm, const int32_t* valid, 
 // uploaded), its row tables in the range's share of each table region, then
 // the frontend and encoder on the range's workspace slice.
 w2v2_status true_length_rows(w2v2_model* m, const float* pcm, int b0, int nb, const int64_t* P, float* logits,
-                             hipStream_t s) {
+                             hipStream_t s, bool shared = false) {
   const w2v2_config& c = m->cfg;
   const int n = c.n_conv, Bm = c.max_batch;
   const int32_t* dlen = m->tl_i32;
@@ -1010,7 +1012,8 @@ w2v2_status true_length_rows(w2v2_model* m, const float* pcm, int b0, int nb, co
   tmax = std::max(tmax, Tf);
   W2V2_LAUNCH(m, s, "row_tables", launch_row_tables(tabs, nt, nb, tmax, s));
 
-  const Ws w = ws_rows(m, b0);
+  Ws w = ws_rows(m, b0);
+  w.shared = shared;
   const void* feat = nullptr;
   W2V2_TRY(run_frontend(m, w, pcm + (size_t)b0 * c.window, dvalid + b0, nb, s, &feat, &pk));
   return run_encoder(m, w, feat, nb, logits + (size_t)b0 * Tf * c.vocab, s, &pk);
@@ -1093,7 +1096,7 @@ w2v2_status w2v2_forward_true_length(w2v2_model* m, const float* pcm, const int3
         return fail(W2V2_E_DEVICE, "fork of the streams failed");
     w2v2_status st = W2V2_OK;
     for (int p = 0; p < np && st == W2V2_OK; ++p)
-      st = true_length_rows(m, pcm, r0[p], r0[p + 1] - r0[p], P[p], logits, p == 0 ? s : m->aux[p]);
+      st = true_length_rows(m, pcm, r0[p], r0[p + 1] - r0[p], P[p], logits, p == 0 ? s : m->aux[p], true);
     for (int p = 1; p < np; ++p)
       if (hipEventRecord(m->ev_join[p], m->aux[p]) != hipSuccess || hipStreamWaitEvent(s, m->ev_join[p], 0) != hipSuccess)
         return fail(W2V2_E_DEVICE, "join of the streams failed");

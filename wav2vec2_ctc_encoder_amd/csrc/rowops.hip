@@ -16,11 +16,7 @@ namespace {
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
+__device__ inline float wave_sum(float v) { return wave_sum64(v); }
 
 template <typename T>
 __device__ inline float4 load4(const T* p);

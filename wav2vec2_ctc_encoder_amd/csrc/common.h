@@ -149,7 +149,9 @@ struct GemmArgs {
   int32_t act = 0;  // 0 none, 1 erf GELU, 2 tanh GELU (applied after the bias)
 };
 
-// Tile shape is chosen from N: 128x32, 128x48, 128x64 or 128x128.
+// fp16 with K % 64 == 0 and N > 32: 128x128 or 128x64 tiles of the direct-to-LDS
+// kernel (chosen from N, K and the tile count); otherwise 128xN tiles (N = 32,
+// 48, 64, 128) of the register-staged kernel.
 hipError_t launch_gemm(DType t, const GemmArgs& a, hipStream_t s);
 
 // ----------------------------------------------------------------------------

@@ -674,7 +674,7 @@ hipError_t launch_shape(const GemmArgs& a, hipStream_t s) {
       return launch_dlds<128, 64, ROLE, 3>(a, s);
     }
   }
-  if (a.N <= 32) return launch_t<T, 128, 32, 4, 1, ROLE>(a, s);
+  if (a.N <= 32) return launch_t<T, 64, 32, 4, 1, ROLE>(a, s);
   if (a.N <= 48) return launch_t<T, 128, 48, 4, 1, ROLE>(a, s);
   if (a.N <= 64) return launch_t<T, 128, 64, 4, 1, ROLE>(a, s);
   return launch_t<T, 128, 128, 2, 2, ROLE>(a, s);

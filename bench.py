@@ -154,8 +154,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
-              "(utterances are independent, see the sharding notes in the design document)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not implemented (windows are independent, "
+              "so a multi-GPU run would split the batch across GPUs with no communication)", file=sys.stderr)
         return 2
 
     import torch

@@ -390,9 +390,10 @@ __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restric
 }
 
 // shared: another part of the batch runs concurrently.  The kernel then asks
-// for enough (unused) dynamic LDS that at most two of its workgroups share a
-// CU, which leaves room for a GEMM workgroup (64 KB) of the other part; with
-// the GPU to itself it takes up to three per CU.
+// for enough (unused) dynamic LDS (56 KB per workgroup) that at most two of
+// its workgroups share a CU, leaving the rest of the CU (48 KB of LDS, one
+// 128x64 GEMM workgroup) to the other part; with the GPU to itself it takes
+// up to three per CU.
 template <int DH, int NW>
 hipError_t launch_a16(const void* qkv, void* out, int B, int Tn, RowSpan rows, int H, bool shared, hipStream_t s) {
   const float c1 = 1.4426950408889634f / sqrtf((float)DH);

@@ -158,6 +158,26 @@ def test_row_bits_do_not_depend_on_the_batch():
     assert np.array_equal(odd, whole[1:6])
 
 
+def test_true_length_split_matches_one_pass():
+    # batch >= 2 packs and runs its halves concurrently; profiling every kernel
+    # runs all rows as one packed pass on one stream: the bits must agree
+    import wav2vec2_ctc_encoder_amd as w2
+    cfg = synth.BASE_10S_B1.replace(batch=5, layers=2)
+    valid = np.array([160000, 20000, 0, 99999, 400], np.int32)
+    pcm = _pcm(cfg, valid)
+    _say(f"true-length split vs one pass, valid {valid.tolist()}")
+    with w2.Model(cfg, _weights(cfg), max_batch=5) as m:
+        tp = torch.from_numpy(pcm).cuda()
+        split, vf_split = m.forward_true_length(tp, valid)
+        m.profile_enable(True)
+        one, vf_one = m.forward_true_length(tp, valid)
+        torch.cuda.synchronize()
+        m.profile_read()
+        m.profile_enable(False)
+        assert torch.equal(vf_split, vf_one)
+        assert torch.equal(split, one)
+
+
 def test_full_rows_equal_padded_mode_bitwise():
     import wav2vec2_ctc_encoder_amd as w2
     cfg = synth.BASE_10S_B1.replace(batch=2, layers=2)

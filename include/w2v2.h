@@ -219,6 +219,25 @@ w2v2_status w2v2_forward(w2v2_model* model, const float* pcm, const int32_t* val
                          float* logits, int32_t* vframes, void* stream);
 
 /*
+ * Whole network plus greedy CTC decoding in one call: w2v2_forward followed
+ * by the decoding of w2v2_ctc_greedy ([TRT] "Method": per-frame argmax, CTC
+ * token ids), with the per-frame argmax taken inside the CTC head's GEMM
+ * epilogue from the fp32 values it stores, so the logits are not read back.
+ *   pcm, valid, batch, logits  as in w2v2_forward (logits are still written).
+ *   vframes  dev int32 [batch]: frames decoded per row (required).
+ *   ids      dev int32 [batch, T]: ids[b, 0 .. lens[b]) are the tokens of row
+ *            b (runs of equal per-frame argmax merged, blank_id dropped), the
+ *            rest -1.
+ *   lens     dev int32 [batch].
+ * The argmax takes the lowest index on ties (-0 and +0 are equal), so ids and
+ * lens are bit-identical to w2v2_ctc_greedy applied to the logits.  Same
+ * execution and stream rules as w2v2_forward; allocates nothing.
+ * Errors: as w2v2_forward, plus W2V2_E_ARG if vframes, ids or lens is NULL.
+ */
+w2v2_status w2v2_forward_greedy(w2v2_model* model, const float* pcm, const int32_t* valid, int32_t batch,
+                                float* logits, int32_t* vframes, int32_t* ids, int32_t* lens, void* stream);
+
+/*
  * Whole network with every row taken as its own true-length clip ([TRT]
  * "Wav2Vec2 CTC layouts": true-length PCM input, no padded-batch attention
  * mask): row b is computed exactly as a single clip of its first valid[b]
@@ -296,7 +315,13 @@ w2v2_status w2v2_ctc_greedy(const float* logits, const int32_t* vframes, int32_t
  * launch).  Without `only`, w2v2_forward runs the whole batch as one pass
  * on the caller's stream, so every timed kernel runs alone; with `only` it
  * keeps the two halves concurrent, and a timed launch then shares the GPU
- * with the other half's kernels.
+ * with the other half's kernels.  `only` = "stage" times no kernel but
+ * records, for every part of the batch that w2v2_forward / w2v2_forward_greedy
+ * runs (the two concurrent halves), one pair around its conv frontend
+ * ("stage_frontend") and one around its encoder and CTC head
+ * ("stage_encoder") on the part's stream: the frontend / encoder boundary of
+ * the unchanged concurrent execution ([LiteRT] "Rewrites for the GPU",
+ * two-graph split).
  * w2v2_profile_read synchronizes on the recorded events, accumulates the
  * per-kernel-name totals since the last read, and writes up to `cap`
  * entries: names[i] (static strings owned by the library), total_ms[i] and

@@ -368,3 +368,121 @@ def test_two_stream_split_matches_one_pass(batch):
         m.profile_enable(False)
         assert torch.equal(vf_split, vf_one)
         assert torch.equal(split, one)
+
+
+# ----------------------------------------------------------------------------
+# forward + decode in one call (argmax inside the CTC head's epilogue)
+# ----------------------------------------------------------------------------
+def _fused_vs_separate(cfg, W, pcm, valid, precision=None):
+    import wav2vec2_ctc_encoder_amd as w2
+    with w2.Model(cfg, W, max_batch=pcm.shape[0], precision=precision) as m:
+        tp, tv = torch.from_numpy(pcm).cuda(), torch.from_numpy(valid).cuda()
+        lg, vf = m.forward(tp, tv)
+        ids, lens = w2.ctc_greedy(lg, vf, blank_id=cfg.blank_id)
+        lg2, vf2, ids2, lens2 = m.forward_greedy(tp, tv)
+        torch.cuda.synchronize()
+        assert torch.equal(lg, lg2)
+        assert torch.equal(vf, vf2)
+        assert torch.equal(lens, lens2)
+        assert torch.equal(ids, ids2)
+        return lg2.cpu().numpy(), vf2.cpu().numpy(), ids2.cpu().numpy(), lens2.cpu().numpy()
+
+
+# the head's three epilogue paths: 16x16 register-staged kernel (N <= 32 or
+# fp32), the 32x32 kernel's LDS-staged epilogue (N % 8 == 0) and its direct
+# epilogue (N = 2341)
+_FUSED_TINY = {
+    "v32_fp32": (_TINY, "fp32"),
+    "v32_fp16": (_TINY, "fp16"),
+    "v256_fp16_staged": (_TINY.replace(vocab=256, batch=3, valid_range=(400, 16000)), "fp16"),
+    "v2341_fp16_direct": (_TINY.replace(vocab=2341, batch=2, valid_range=(6000, 16000)), "fp16"),
+    "v2341_fp32": (_TINY.replace(vocab=2341, batch=2, valid_range=(6000, 16000)), "fp32"),
+}
+
+
+@pytest.mark.parametrize("variant", sorted(_FUSED_TINY))
+def test_forward_greedy_tiny_matches_separate_decode(variant):
+    cfg, prec = _FUSED_TINY[variant]
+    _say(f"forward_greedy tiny {variant}")
+    W, pcm, valid = _inputs(cfg)
+    lg, vf, ids, lens = _fused_vs_separate(cfg, W, pcm, valid, prec)
+    _check_ids(cfg, lg, vf, ids, lens)
+
+
+@pytest.mark.parametrize("name", ["base_10s_b1", "base_16s_b8", "large_16s_b4", "base_16s_b32"])
+def test_forward_greedy_full_workloads_match_separate_decode(name):
+    cfg = synth.PRESETS[name]
+    _say(f"forward_greedy {name}")
+    W, pcm, valid = _inputs(cfg)
+    _fused_vs_separate(cfg, W, pcm, valid)
+
+
+@pytest.mark.parametrize("prec", ["fp32", "fp16"])
+@pytest.mark.parametrize("vocab", [32, 2341])
+def test_forward_greedy_exact_ties_and_signed_zeros(prec, vocab):
+    """Zero head weight: every frame's logits equal the head bias exactly.
+    The bias holds its maximum three times and -0 / +0 side by side, so the
+    argmax must be the first maximum; with the maximum at 0 (-0 first) the
+    -0 and +0 entries tie."""
+    cfg = _TINY.replace(vocab=vocab, batch=2, valid_range=(9000, 16000))
+    W, pcm, valid = _inputs(cfg)
+    for top, first in ((3.0, 5), (0.0, 2)):
+        _say(f"forward_greedy ties {prec} V={vocab} max={top}")
+        W2 = dict(W)
+        W2["head.weight"] = np.zeros_like(W["head.weight"])
+        bias = np.full(vocab, -1.0, np.float32)
+        if top > 0:
+            bias[[5, 9, vocab - 1]] = top
+            bias[2] = -0.0
+            bias[7] = 0.0
+        else:
+            bias[2] = -0.0
+            bias[7] = 0.0
+            bias[vocab - 3] = 0.0
+        W2["head.bias"] = bias
+        lg, vf, ids, lens = _fused_vs_separate(cfg, W2, pcm, valid, prec)
+        a = oracle.frame_argmax(lg)
+        assert np.all(a[:, :] == first), np.unique(a)
+        for b in range(cfg.batch):
+            assert lens[b] == (1 if vf[b] > 0 else 0)
+            if vf[b] > 0:
+                assert ids[b, 0] == first
+
+
+@pytest.mark.parametrize("name,batch", [("base_10s_b1", 1), ("base_10s_b1", 3)])
+def test_forward_greedy_graph_replays_match_eager(name, batch):
+    """forward_greedy captured once into a HIP graph (one stream for batch 1,
+    the forked second stream for batch 3) and replayed several times, with
+    eager calls on other inputs and synchronizations between the replays:
+    every replay gives the eager call's exact logits and ids."""
+    import wav2vec2_ctc_encoder_amd as w2
+    cfg = synth.PRESETS[name].replace(batch=batch, layers=2, valid_range=(20000, 160000), pcm_seed=909)
+    _say(f"graph replay forward_greedy {name} batch {batch}")
+    W, pcm, valid = _inputs(cfg)
+    other = np.flip(pcm, axis=1).copy()  # other samples, same valid lengths
+    with w2.Model(cfg, W, max_batch=batch) as m:
+        tp, tv = torch.from_numpy(pcm).cuda(), torch.from_numpy(valid).cuda()
+        to = torch.from_numpy(other).cuda()
+        ref = [t.clone() for t in m.forward_greedy(tp, tv)]
+        bufs = [torch.empty_like(t) for t in ref]
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            m.forward_greedy(tp, tv, *bufs)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            m.forward_greedy(tp, tv, *bufs)
+        torch.cuda.synchronize()
+        for it in range(4):
+            for b in bufs:
+                b.fill_(-7)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for r, b in zip(ref, bufs):
+                assert torch.equal(r, b), it
+            # eager work on other inputs between the replays
+            m.forward_greedy(to, tv)
+            torch.cuda.synchronize()

@@ -152,6 +152,29 @@ class Model:
                                            _stream(stream)), "w2v2_forward")
         return logits, vframes
 
+    def forward_greedy(self, pcm: torch.Tensor, valid: torch.Tensor, logits: torch.Tensor | None = None,
+                       vframes: torch.Tensor | None = None, ids: torch.Tensor | None = None,
+                       lens: torch.Tensor | None = None, stream=None):
+        """Forward plus greedy CTC decoding in one call (``w2v2_forward_greedy``):
+        the CTC head's epilogue takes each frame's argmax, so the logits are not
+        read again.  Returns (logits, vframes, ids, lens)."""
+        B = pcm.shape[0]
+        _need(pcm, torch.float32, (B, self.window), "pcm")
+        _need(valid, torch.int32, (B,), "valid")
+        T = self.frames_per_window
+        dev = pcm.device
+        logits = torch.empty(B, T, self.vocab, dtype=torch.float32, device=dev) if logits is None else logits
+        vframes = torch.empty(B, dtype=torch.int32, device=dev) if vframes is None else vframes
+        ids = torch.empty(B, T, dtype=torch.int32, device=dev) if ids is None else ids
+        lens = torch.empty(B, dtype=torch.int32, device=dev) if lens is None else lens
+        _need(logits, torch.float32, (B, T, self.vocab), "logits")
+        _need(vframes, torch.int32, (B,), "vframes")
+        _need(ids, torch.int32, (B, T), "ids")
+        _need(lens, torch.int32, (B,), "lens")
+        _lib.check(_lib.lib().w2v2_forward_greedy(self._h, _ptr(pcm), _ptr(valid), B, _ptr(logits), _ptr(vframes),
+                                                  _ptr(ids), _ptr(lens), _stream(stream)), "w2v2_forward_greedy")
+        return logits, vframes, ids, lens
+
     def forward_true_length(self, pcm: torch.Tensor, valid, logits: torch.Tensor | None = None,
                             vframes: torch.Tensor | None = None, stream=None):
         """Every row as its own true-length clip of valid[b] samples.

@@ -147,7 +147,29 @@ struct GemmArgs {
   void* out_t = nullptr;
   int64_t ldc = 0, c_group = 0;
   int32_t act = 0;  // 0 none, 1 erf GELU, 2 tanh GELU (applied after the bias)
+  // Optional per-row argmax (CTC head): for every output row r (r = m, or
+  // c_rows[m] / ldc with an output row table) amax[r] is raised with
+  // atomicMax to the largest argmax_key of the row's stored fp32 values, so
+  // after the launch it holds the row's maximum and its lowest column.  The
+  // caller zero-fills amax first.
+  uint64_t* amax = nullptr;
 };
+
+// Argmax key of value v in column n: a larger value gives a larger key, and
+// equal values give the larger key to the lower column, so the maximum key of
+// a row names its first maximum (numpy's argmax convention) whatever order
+// the keys are combined in.  -0 counts as +0 (they compare equal); the low
+// word is 0xFFFFFFFF - n, so n = 0xFFFFFFFF - (uint32_t)key.
+__device__ inline uint64_t argmax_key(float v, int n) {
+  const uint32_t u = v == 0.f ? 0u : __float_as_uint(v);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
+}
+__device__ inline uint64_t max_key_xor(uint64_t k, int mask) {
+  const uint32_t lo = __shfl_xor((uint32_t)k, mask, 64), hi = __shfl_xor((uint32_t)(k >> 32), mask, 64);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > k ? o : k;
+}
 
 // fp16 with K % 64 == 0 and N > 32: 128x128 or 128x64 tiles of the direct-to-LDS
 // kernel (chosen from N, K and the tile count); otherwise 128xN tiles (N = 32,
@@ -243,5 +265,10 @@ hipError_t launch_frame_argmax(const float* logits, int64_t rows, int32_t V, int
                                hipStream_t s);
 hipError_t launch_ctc_collapse(const int32_t* vframes, int32_t B, int32_t T, int32_t blank,
                                int32_t* ids, int32_t* lens, hipStream_t s);
+// The same collapse over paths given as argmax keys (argmax_key) [B, T].
+hipError_t launch_ctc_collapse_keys(const uint64_t* keys, const int32_t* vframes, int32_t B, int32_t T,
+                                    int32_t blank, int32_t* ids, int32_t* lens, hipStream_t s);
+// keys [n] = 0 (before an argmax-raising GEMM)
+hipError_t launch_zero_keys(uint64_t* keys, int64_t n, hipStream_t s);
 
 }  // namespace w2v2

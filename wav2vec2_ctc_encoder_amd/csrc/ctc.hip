@@ -6,7 +6,10 @@
 // (value, index) pairs are merged with the lowest index winning ties, so the
 // result equals numpy's first-maximum argmax whatever the reduction order.
 // ctc_collapse: one workgroup per row; the row's argmax path is first copied
-// to LDS, so the compaction can write the ids in place over it.
+// to LDS, so the compaction can write the ids in place over it.  The path
+// comes either from frame_argmax (in ids) or from the per-frame argmax keys
+// that the CTC head's GEMM epilogue raises (argmax_key in common.h), which
+// saves the second pass over the [B, T, V] logits.
 #include <limits.h>
 
 #include "common.h"
@@ -48,14 +51,21 @@ __global__ __launch_bounds__(256) void frame_argmax_kernel(const float* __restri
   if (lane == 0) out[row] = (bi == INT_MAX) ? 0 : bi;
 }
 
-__global__ __launch_bounds__(1024) void ctc_collapse_kernel(const int32_t* __restrict__ vframes, int T, int blank,
+// keys == null: the argmax path is in ids (frame_argmax wrote it there);
+// otherwise it is given by the argmax keys (see argmax_key) of each frame.
+__global__ __launch_bounds__(1024) void ctc_collapse_kernel(const uint64_t* __restrict__ keys,
+                                                            const int32_t* __restrict__ vframes, int T, int blank,
                                                             int32_t* ids, int32_t* __restrict__ lens) {
   extern __shared__ int32_t path[];  // [T]
   __shared__ int32_t wtot[16];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t* row = ids + (int64_t)b * T;
-  for (int t = tid; t < T; t += 1024) path[t] = row[t];
+  if (keys) {
+    for (int t = tid; t < T; t += 1024) path[t] = (int32_t)(0xFFFFFFFFu - (uint32_t)keys[(int64_t)b * T + t]);
+  } else {
+    for (int t = tid; t < T; t += 1024) path[t] = row[t];
+  }
   int vf = vframes[b];
   vf = vf < 0 ? 0 : (vf > T ? T : vf);
   __syncthreads();
@@ -88,6 +98,12 @@ __global__ __launch_bounds__(1024) void ctc_collapse_kernel(const int32_t* __res
   if (tid == 0) lens[b] = offset;
 }
 
+// Argmax slots start at 0, below every key, before a GEMM raises them (a
+// fill kernel, not a memset, so that the forward can be graph-captured).
+__global__ __launch_bounds__(256) void zero_keys_kernel(uint64_t* __restrict__ keys, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) keys[i] = 0;
+}
+
 }  // namespace
 
 hipError_t launch_frame_argmax(const float* logits, int64_t rows, int32_t V, int32_t* out, hipStream_t s) {
@@ -99,8 +115,23 @@ hipError_t launch_frame_argmax(const float* logits, int64_t rows, int32_t V, int
 hipError_t launch_ctc_collapse(const int32_t* vframes, int32_t B, int32_t T, int32_t blank, int32_t* ids,
                                int32_t* lens, hipStream_t s) {
   if (B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ctc_collapse_kernel, dim3(B), dim3(1024), (size_t)T * sizeof(int32_t), s, vframes, T, blank,
-                     ids, lens);
+  hipLaunchKernelGGL(ctc_collapse_kernel, dim3(B), dim3(1024), (size_t)T * sizeof(int32_t), s, nullptr, vframes, T,
+                     blank, ids, lens);
+  return hipGetLastError();
+}
+
+hipError_t launch_ctc_collapse_keys(const uint64_t* keys, const int32_t* vframes, int32_t B, int32_t T,
+                                    int32_t blank, int32_t* ids, int32_t* lens, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ctc_collapse_kernel, dim3(B), dim3(1024), (size_t)T * sizeof(int32_t), s, keys, vframes, T,
+                     blank, ids, lens);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_keys(uint64_t* keys, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t g = (n + 255) / 256;
+  hipLaunchKernelGGL(zero_keys_kernel, dim3((unsigned)(g < 65535 ? g : 65535)), dim3(256), 0, s, keys, n);
   return hipGetLastError();
 }
 

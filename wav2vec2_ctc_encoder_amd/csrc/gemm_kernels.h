@@ -1,0 +1,744 @@
+// MFMA GEMM kernels for gfx950 with a row-mapped A operand and a fused epilogue.
+//
+// Serves every dense contraction of the network:
+//  * the encoder linears (fused QKV, out, FFN1, FFN2), the feature projection
+//    and the CTC head (plain rows: seg_rows = M, lda = K);
+//  * the strided feature-encoder convs as implicit GEMM: in the channels-last
+//    layout [B, T_in, C] the input window of output frame t is the contiguous
+//    run of k*C elements starting at frame s*t, so A row (b, t) begins at
+//    b*T_in*C + t*s*C (seg = b, lda = s*C, K = k*C) and the weight is the
+//    conv kernel repacked to [C_out, k*C] with K index j*C + c;
+//  * the grouped positional conv, one grid.z slice per group, over a
+//    zero-padded per-group copy of its input (lda = C_g, K = taps*C_g).
+//
+// Two kernels, both 256 threads = 4 waves with the weight as the MFMA A
+// operand (n side) and the activation as the B operand (m side), so a lane
+// holds consecutive output columns of one row:
+//
+// gemm_dlds_kernel (fp16, K % 64 == 0, N > 32; the hot path): block tile
+//   128x128 or 128x64, waves 2 x 2, v_mfma_f32_32x32x16_f16.  K advances in
+//   64-wide steps through two LDS buffers filled by wave-wide direct
+//   global->LDS loads (global_load_lds_dwordx4, 16 bytes per lane) into
+//   XOR-swizzled 128-byte rows; explicit vmcnt waits, one barrier per step.
+//   All MFMA fragments of the next step are read from LDS into registers
+//   while the current step's MFMAs run, so no MFMA waits on an LDS read.
+//   Epilogue: bias and activation in registers, then each wave stages its
+//   32-row slabs row-major in LDS and writes whole rows (residual add, fp32
+//   and/or fp16 stores), because the 32x32 accumulator layout would
+//   otherwise scatter 16-byte pieces over 32 rows per store.
+//
+// gemm_kernel (fp32 mode and the remaining shapes): block tile BM x BN, K
+//   step of 128 bytes per row (64 fp16 / 32 fp32), double-buffered LDS with
+//   the next K step prefetched into registers, one barrier per step; each
+//   wave owns a (TN*16) x (TM*16) sub-tile of 16x16 MFMA blocks and stores
+//   16-byte (fp32) / 8-byte (fp16) vectors.
+//   fp16: v_mfma_f32_16x16x32_f16, one per 16-byte lane fragment.
+//   fp32: v_mfma_f32_16x16x4_f32, four per 16-byte lane fragment; fragment
+//         element j of lane group g carries k = 4g + j for both operands, a
+//         permutation of the 16 k values, so the sum is unchanged.
+//
+// A rows come from the segment rule above or, for packed true-length rows,
+// from a per-row offset table; output rows likewise (c_rows).
+//
+// This header holds the kernels and their launch shapes; every GEMM role is
+// instantiated in its own translation unit (gemm_role_*.hip), so the roles
+// compile in parallel.
+#pragma once
+#include "common.h"
+
+namespace w2v2 {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPitch = 9;  // LDS row pitch in 16-byte units: 128 B of data + 16 B pad
+
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<half_t> {
+  __device__ static inline void run(const uint4& a, const uint4& b, f4& c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b),
+                                               c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma<float> {
+  __device__ static inline void run(const uint4& a, const uint4& b, f4& c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  }
+};
+
+
+
+// Spread consecutive workgroups of one XCD over a contiguous range of tiles:
+// the dispatcher hands workgroup ids to the 8 XCDs round-robin, and each XCD
+// has its own L2, so neighbouring tiles (which share A rows or B columns)
+// should land on the same XCD.
+__device__ inline int xcd_remap(int pid, int nb) {
+  const int x = pid & 7, local = pid >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  return x * per + (x < rem ? x : rem) + local;
+}
+
+// Residual element(s) of logical row m. With res_stats set, the residual
+// buffer holds a raw sum whose LayerNorm (row statistics res_stats[m], affine
+// res_gamma/res_beta) is applied here as it is read.
+__device__ inline float4 residual4(const GemmArgs& a, int m, int n, const float* r) {
+  float4 v = *(const float4*)r;
+  if (a.res_stats) {
+    const float2 st = a.res_stats[m];
+    const float4 g = *(const float4*)(a.res_gamma + n), b = *(const float4*)(a.res_beta + n);
+    v.x = (v.x - st.x) * st.y * g.x + b.x;
+    v.y = (v.y - st.x) * st.y * g.y + b.y;
+    v.z = (v.z - st.x) * st.y * g.z + b.z;
+    v.w = (v.w - st.x) * st.y * g.w + b.w;
+  }
+  return v;
+}
+__device__ inline float residual1(const GemmArgs& a, int m, int n, float r) {
+  if (a.res_stats) {
+    const float2 st = a.res_stats[m];
+    r = (r - st.x) * st.y * a.res_gamma[n] + a.res_beta[n];
+  }
+  return r;
+}
+
+// Epilogue for 4 consecutive output columns nb..nb+3 of row m:
+// v = acc + bias; v = act(v); v += residual; store fp32 and/or operand type.
+// Returns the values stored (entries of columns >= N are unspecified).
+template <typename T, int ACT>
+__device__ inline f4 epilogue4(const GemmArgs& a, const float* bias, int m, int64_t rowoff, int nb, f4 v,
+                               bool vec) {
+  if (vec) {
+    if (bias) {
+      const float4 bb = *(const float4*)(bias + nb);
+      v.x += bb.x; v.y += bb.y; v.z += bb.z; v.w += bb.w;
+    }
+    v.x = act_fn<ACT>(v.x); v.y = act_fn<ACT>(v.y); v.z = act_fn<ACT>(v.z); v.w = act_fn<ACT>(v.w);
+    if (a.residual) {
+      const float4 rr = residual4(a, m, nb, a.residual + rowoff + nb);
+      v.x += rr.x; v.y += rr.y; v.z += rr.z; v.w += rr.w;
+    }
+    if (a.out_f32) *(float4*)(a.out_f32 + rowoff + nb) = make_float4(v.x, v.y, v.z, v.w);
+    if (a.out_t) {
+      if constexpr (sizeof(T) == 2) {
+        h4 hv = {(half_t)v.x, (half_t)v.y, (half_t)v.z, (half_t)v.w};
+        *(h4*)((half_t*)a.out_t + rowoff + nb) = hv;
+      } else {
+        *(float4*)((float*)a.out_t + rowoff + nb) = make_float4(v.x, v.y, v.z, v.w);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = nb + r;
+      if (n >= a.N) break;
+      float x = v[r];
+      if (bias) x += bias[n];
+      x = act_fn<ACT>(x);
+      if (a.residual) x += residual1(a, m, n, a.residual[rowoff + n]);
+      if (a.out_f32) a.out_f32[rowoff + n] = x;
+      if (a.out_t) ((T*)a.out_t)[rowoff + n] = (T)x;
+      v[r] = x;
+    }
+  }
+  return v;
+}
+
+// Largest argmax key over the valid columns nb..nb+3 of one row's values.
+__device__ inline uint64_t best_key4(const f4& v, int nb, int N, uint64_t k) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t c = argmax_key(v[r], nb + r);
+    if (nb + r < N && c > k) k = c;
+  }
+  return k;
+}
+// Output row of logical row m (the argmax slot of that row).
+__device__ inline int64_t amax_row(const GemmArgs& a, int m) { return a.c_rows ? a.c_rows[m] / a.ldc : m; }
+
+template <int N>
+struct ActTag {
+  static constexpr int value = N;
+};
+
+// Element offset of A row m (before the group offset) and of output row m.
+__device__ inline int64_t a_row_offset(const GemmArgs& a, int m) {
+  if (a.a_rows) return a.a_rows[m];
+  const int seg = m / a.seg_rows, t = m - seg * a.seg_rows;
+  return (int64_t)seg * a.a_seg + (int64_t)t * a.lda;
+}
+__device__ inline int64_t c_row_offset(const GemmArgs& a, int m) {
+  return a.c_rows ? a.c_rows[m] : (int64_t)m * a.ldc;
+}
+
+__device__ inline bool epilogue_vec_ok(const GemmArgs& a) {
+  return ((a.ldc & 3) == 0) && ((a.N & 3) == 0) && ((a.c_group & 3) == 0) && ((a.bias_group & 3) == 0);
+}
+
+typedef float f16x __attribute__((ext_vector_type(16)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+
+// Whole 8-column chunks everywhere: the staged epilogue below stores 16 B of
+// fp16 (32 B of fp32) per lane.
+__device__ inline bool epilogue_staged_ok(const GemmArgs& a) {
+  const uintptr_t ptrs = (uintptr_t)a.out_t | (uintptr_t)a.out_f32 | (uintptr_t)a.residual | (uintptr_t)a.bias |
+                         (uintptr_t)a.res_gamma | (uintptr_t)a.res_beta;
+  return ((a.ldc & 7) == 0) && ((a.N & 7) == 0) && ((a.c_group & 7) == 0) && ((a.bias_group & 7) == 0) &&
+         ((ptrs & 15) == 0);
+}
+
+// Epilogue of one wave's (TM*32) x (TN*32) block of 32x32 MFMA accumulators
+// (lane l holds, for block (i, j), rows m = j*32 + l%32 and the 4 columns
+// n = i*32 + 8q + 4*(l/32) + 0..3 in elements 4q..4q+3).  That layout makes
+// direct stores scatter 16-byte pieces over 32 rows per instruction, so each
+// 32-row slab goes through the wave's own LDS region instead: bias and the
+// activation are applied in registers, the slab is written row-major (row
+// pitch padded by 16 bytes to spread the rows over the banks) and read back
+// with LPR consecutive lanes covering one row, so the residual loads and the
+// output stores move whole contiguous rows.  LDS operations of one wave run in
+// order, so no barrier is needed between the write and the read-back.
+// NT: non-temporal output stores (conv outputs: hundreds of MB written once
+// and read once by the next layer; keeping them out of the caches leaves the
+// L2 to the operand tiles).
+template <int TM, int TN, int ACT, bool NT>
+__device__ inline void epilogue_staged(const GemmArgs& a, f16x (&acc)[TN][TM], float* stage, int m_base,
+                                       int n_base, int group) {
+  constexpr int W = TN * 32;     // columns of the wave block
+  constexpr int P = W + 4;       // padded row pitch (floats)
+  constexpr int LPR = W / 8;     // lanes per row in the read-back
+  constexpr int RPP = 64 / LPR;  // rows per read-back pass
+  constexpr int NPS = 32 / RPP;  // read-back passes per 32-row slab
+  const int lane = threadIdx.x & 63, l32 = lane & 31, lg = lane >> 5;
+  const float* bias = a.bias ? a.bias + (int64_t)group * a.bias_group : nullptr;
+  const int64_t cg = (int64_t)group * a.c_group;
+  const int rrow = lane / LPR, rcol = (lane % LPR) * 8;
+  // Operands that do not depend on the row are loaded once, and every load
+  // goes to a clamped in-bounds address without a branch, so the loads issue
+  // together instead of each waiting behind the math of the previous chunk
+  // (N % 8 == 0 here; values of clamped columns or rows are never stored).
+  float4 bv[TN][4];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      bv[i][q] = bias ? *(const float4*)(bias + min(n_base + i * 32 + 8 * q + 4 * lg, a.N - 4))
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  const int nr = min(n_base + rcol, a.N - 8);  // the lane's 8 read-back columns
+  float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0, e0 = g0, e1 = g0;
+  if (a.res_stats) {
+    g0 = *(const float4*)(a.res_gamma + nr);
+    g1 = *(const float4*)(a.res_gamma + nr + 4);
+    e0 = *(const float4*)(a.res_beta + nr);
+    e1 = *(const float4*)(a.res_beta + nr + 4);
+  }
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    // this slab's residual rows, requested before its activation math
+    float4 r0[NPS], r1[NPS];
+    float2 rs[NPS];
+    if (a.residual) {
+#pragma unroll
+      for (int ps = 0; ps < NPS; ++ps) {
+        const int m = min(m_base + j * 32 + ps * RPP + rrow, a.M - 1);
+        const float* r = a.residual + cg + c_row_offset(a, m) + nr;
+        r0[ps] = *(const float4*)r;
+        r1[ps] = *(const float4*)(r + 4);
+        rs[ps] = a.res_stats ? a.res_stats[m] : make_float2(0.f, 1.f);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = i * 32 + 8 * q + 4 * lg;
+        float4 v = make_float4(acc[i][j][4 * q] + bv[i][q].x, acc[i][j][4 * q + 1] + bv[i][q].y,
+                               acc[i][j][4 * q + 2] + bv[i][q].z, acc[i][j][4 * q + 3] + bv[i][q].w);
+        v.x = act_fn<ACT>(v.x); v.y = act_fn<ACT>(v.y); v.z = act_fn<ACT>(v.z); v.w = act_fn<ACT>(v.w);
+        *(float4*)(stage + l32 * P + nl) = v;
+      }
+    }
+#pragma unroll
+    for (int ps = 0; ps < NPS; ++ps) {
+      const int row = ps * RPP + rrow;
+      const int m = m_base + j * 32 + row, n = n_base + rcol;
+      float4 x0 = *(const float4*)(stage + row * P + rcol);
+      float4 x1 = *(const float4*)(stage + row * P + rcol + 4);
+      if (a.residual) {
+        float4 u0 = r0[ps], u1 = r1[ps];
+        if (a.res_stats) {
+          // the residual's LayerNorm: (r - mean) * rstd * gamma + beta
+          const float mu = rs[ps].x, rstd = rs[ps].y;
+          u0.x = (u0.x - mu) * rstd * g0.x + e0.x; u0.y = (u0.y - mu) * rstd * g0.y + e0.y;
+          u0.z = (u0.z - mu) * rstd * g0.z + e0.z; u0.w = (u0.w - mu) * rstd * g0.w + e0.w;
+          u1.x = (u1.x - mu) * rstd * g1.x + e1.x; u1.y = (u1.y - mu) * rstd * g1.y + e1.y;
+          u1.z = (u1.z - mu) * rstd * g1.z + e1.z; u1.w = (u1.w - mu) * rstd * g1.w + e1.w;
+        }
+        x0.x += u0.x; x0.y += u0.y; x0.z += u0.z; x0.w += u0.w;
+        x1.x += u1.x; x1.y += u1.y; x1.z += u1.z; x1.w += u1.w;
+      }
+      if (a.amax) {
+        // the LPR consecutive lanes of this row hold its columns of the wave's block
+        const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        uint64_t key = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint64_t c = argmax_key(xv[e], n + e);
+          if (n + e < a.N && c > key) key = c;
+        }
+#pragma unroll
+        for (int o = 1; o < LPR; o <<= 1) key = max_key_xor(key, o);
+        if (m < a.M && (lane % LPR) == 0)
+          atomicMax((unsigned long long*)(a.amax + amax_row(a, m)), (unsigned long long)key);
+      }
+      if (m < a.M && n < a.N) {
+        const int64_t off = cg + c_row_offset(a, m) + n;
+        if (a.out_f32) {
+          const f4 v0 = {x0.x, x0.y, x0.z, x0.w}, v1 = {x1.x, x1.y, x1.z, x1.w};
+          if constexpr (NT) {
+            __builtin_nontemporal_store(v0, (f4*)(a.out_f32 + off));
+            __builtin_nontemporal_store(v1, (f4*)(a.out_f32 + off + 4));
+          } else {
+            *(f4*)(a.out_f32 + off) = v0;
+            *(f4*)(a.out_f32 + off + 4) = v1;
+          }
+        }
+        if (a.out_t) {
+          const h8v hv = {(half_t)x0.x, (half_t)x0.y, (half_t)x0.z, (half_t)x0.w,
+                          (half_t)x1.x, (half_t)x1.y, (half_t)x1.z, (half_t)x1.w};
+          if constexpr (NT) __builtin_nontemporal_store(hv, (h8v*)((half_t*)a.out_t + off));
+          else *(h8v*)((half_t*)a.out_t + off) = hv;
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int ROLE>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
+  constexpr int TM = BM / WM / 16;
+  constexpr int TN = BN / WN / 16;
+  constexpr int EPC = 16 / sizeof(T);   // elements per 16-byte chunk
+  constexpr int BK = 8 * EPC;           // elements per 128-byte tile row
+  constexpr int NLA = (BM * 8 + 255) / 256;
+  constexpr int NLB = (BN * 8 + 255) / 256;
+  static_assert(WM * WN == 4, "4 waves");
+
+  __shared__ uint4 sA[2][BM * kPitch];
+  __shared__ uint4 sB[2][BN * kPitch];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int group = blockIdx.z;
+
+  // tile coordinates: XCD-aware remap, then grouped raster (8 M-tiles per group)
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles_n = (a.N + BN - 1) / BN;
+  const int pid = xcd_remap(blockIdx.x, gridDim.x);
+  constexpr int GM = 8;
+  const int width = GM * tiles_n;
+  const int first_m = (pid / width) * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int tm = first_m + (pid % width) % gsz;
+  const int tn = (pid % width) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const char* Abase = (const char*)a.A + (int64_t)group * a.a_group * sizeof(T);
+  const char* Bbase = (const char*)a.B + (int64_t)group * a.b_group * sizeof(T);
+
+  // per-thread source rows of the tile loads
+  const char* arow[NLA];
+  bool aok[NLA];
+#pragma unroll
+  for (int i = 0; i < NLA; ++i) {
+    const int idx = tid + 256 * i;
+    const int r = idx >> 3;
+    const int m = m0 + r;
+    aok[i] = (idx < BM * 8) && (m < a.M);
+    const int mm = aok[i] ? m : 0;
+    arow[i] = Abase + a_row_offset(a, mm) * sizeof(T) + (idx & 7) * 16;
+  }
+  const char* brow[NLB];
+  bool bok[NLB];
+#pragma unroll
+  for (int i = 0; i < NLB; ++i) {
+    const int idx = tid + 256 * i;
+    const int r = idx >> 3;
+    const int n = n0 + r;
+    bok[i] = (idx < BN * 8) && (n < a.N);
+    brow[i] = Bbase + ((int64_t)(bok[i] ? n : 0) * a.K) * sizeof(T) + (idx & 7) * 16;
+  }
+
+  uint4 ra[NLA], rb[NLB];
+  auto load = [&](int kt) {
+    const int kbase = kt * BK;
+#pragma unroll
+    for (int i = 0; i < NLA; ++i) {
+      const int idx = tid + 256 * i;
+      const bool ok = aok[i] && (kbase + (idx & 7) * EPC < a.K);
+      ra[i] = ok ? *(const uint4*)(arow[i] + (int64_t)kbase * sizeof(T)) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NLB; ++i) {
+      const int idx = tid + 256 * i;
+      const bool ok = bok[i] && (kbase + (idx & 7) * EPC < a.K);
+      rb[i] = ok ? *(const uint4*)(brow[i] + (int64_t)kbase * sizeof(T)) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NLA; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx < BM * 8) sA[buf][(idx >> 3) * kPitch + (idx & 7)] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NLB; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx < BN * 8) sB[buf][(idx >> 3) * kPitch + (idx & 7)] = rb[i];
+    }
+  };
+
+  f4 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (a.K + BK - 1) / BK;
+  load(0);
+  store(0);
+  __syncthreads();
+
+  const int lr = lane & 15, lg = lane >> 4;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      uint4 wv[TN], av[TM];
+#pragma unroll
+      for (int i = 0; i < TN; ++i) wv[i] = sB[cur][(wn * TN * 16 + i * 16 + lr) * kPitch + cc * 4 + lg];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) av[j] = sA[cur][(wm * TM * 16 + j * 16 + lr) * kPitch + cc * 4 + lg];
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) Mma<T>::run(wv[i], av[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) store(cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows m, columns nb .. nb+3
+  const bool vec = epilogue_vec_ok(a);
+  const float* bias = a.bias ? a.bias + (int64_t)group * a.bias_group : nullptr;
+  const int64_t cg = (int64_t)group * a.c_group;
+  auto store_all = [&](auto act_tag) {
+    constexpr int ACT = decltype(act_tag)::value;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int m = m0 + wm * TM * 16 + j * 16 + lr;
+      uint64_t key = 0;
+      if (m < a.M) {
+        const int64_t rowoff = cg + c_row_offset(a, m);
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+          const int nb = n0 + wn * TN * 16 + i * 16 + lg * 4;
+          if (nb < a.N) {
+            const f4 v = epilogue4<T, ACT>(a, bias, m, rowoff, nb, acc[i][j], vec);
+            key = best_key4(v, nb, a.N, key);
+          }
+        }
+      }
+      if (a.amax) {
+        // the 4 lanes (lg) of row m hold its columns of this wave's block
+        key = max_key_xor(max_key_xor(key, 16), 32);
+        if (m < a.M && lg == 0) atomicMax((unsigned long long*)(a.amax + amax_row(a, m)), (unsigned long long)key);
+      }
+    }
+  };
+  if (a.act == 1) store_all(ActTag<1>{});
+  else if (a.act == 2) store_all(ActTag<2>{});
+  else store_all(ActTag<0>{});
+}
+
+// One wave-wide direct global->LDS load: lane l's 16 bytes at gptr land at
+// LDS byte address lds + 16*l.  Written as inline asm so that the compiler's
+// wait-count pass does not treat every later LDS read as dependent on it (it
+// would wait for all outstanding loads, serialising the pipeline); the
+// kernel waits on vmcnt explicitly.  The instruction has no result register;
+// its LDS base is an input bound to m0, so the compiler itself sets m0.
+__device__ inline void dma16(const void* gptr, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds) : "memory");
+}
+
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left at their maxima (no wait).
+// Encoding (gfx9): vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+template <int N>
+__device__ inline void wait_vmcnt_imm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// s_waitcnt lgkmcnt(0): every LDS read of this wave has returned.
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8)); }
+
+// WPE: waves per SIMD the register budget is fitted to (2 for 128x128 tiles,
+// 3 for 128x64, which LDS also allows: 64 / 48 KB per workgroup).
+template <int BM, int BN, int ROLE, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemm_dlds_kernel(GemmArgs a) {
+  constexpr int WM = 2, WN = 2;
+  constexpr int TM = BM / WM / 32;  // 32x32 blocks per wave along m
+  constexpr int TN = BN / WN / 32;  // ... along n
+  constexpr int CPR = 8;            // 16-byte chunks per tile row: 64 fp16 of K per step
+  constexpr int RPI = 64 / CPR;     // tile rows per 1 KB wave load
+  constexpr int KEYDIV = 16 / CPR;  // rows sharing a bank-group phase
+  constexpr int KS = 4;             // 16-wide K slices per step
+  constexpr int JA = BM / RPI / 4;  // 1 KB load instructions per wave per step (A)
+  constexpr int JB = BN / RPI / 4;  // (B)
+  constexpr int LPS = JA + JB;      // loads per thread per step
+  constexpr int ABUF = BM * CPR, BBUF = BN * CPR;  // uint4 per buffer
+  static_assert(TM >= 1 && TN >= 1 && JA >= 1 && JB >= 1 && LPS <= 63, "tile");
+
+  // [A buffer 0][A buffer 1][B buffer 0][B buffer 1]; the epilogue reuses all of it
+  __shared__ uint4 smem[2 * (ABUF + BBUF)];
+  static_assert(4 * 32 * (TN * 32 + 4) * 4 <= 2 * (ABUF + BBUF) * 16, "epilogue staging fits");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int group = blockIdx.z;
+
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles_n = (a.N + BN - 1) / BN;
+  const int pid = xcd_remap(blockIdx.x, gridDim.x);
+  constexpr int GM = 8;
+  const int width = GM * tiles_n;
+  const int first_m = (pid / width) * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int tm = first_m + (pid % width) % gsz;
+  const int tn = (pid % width) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const char* Abase = (const char*)a.A + (int64_t)group * a.a_group * 2;
+  const char* Bbase = (const char*)a.B + (int64_t)group * a.b_group * 2;
+
+  // source rows (clamped) with the swizzled chunk folded in: LDS chunk p of
+  // tile row r holds source chunk p ^ key(r)
+  const int pos = lane & (CPR - 1);
+  const char* asrc[JA];
+#pragma unroll
+  for (int j = 0; j < JA; ++j) {
+    const int r = (wave * JA + j) * RPI + lane / CPR;
+    const int m = min(m0 + r, a.M - 1);
+    asrc[j] = Abase + a_row_offset(a, m) * 2 + ((pos ^ ((r / KEYDIV) & (CPR - 1))) << 4);
+  }
+  const char* bsrc[JB];
+#pragma unroll
+  for (int j = 0; j < JB; ++j) {
+    const int r = (wave * JB + j) * RPI + lane / CPR;
+    const int n = min(n0 + r, a.N - 1);
+    bsrc[j] = Bbase + (int64_t)n * a.K * 2 + ((pos ^ ((r / KEYDIV) & (CPR - 1))) << 4);
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&smem[0];
+  auto issue = [&](int kt, int buf) {
+    const int64_t koff = (int64_t)kt * 128;
+#pragma unroll
+    for (int j = 0; j < JA; ++j)
+      dma16(asrc[j] + koff,
+            __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((buf * ABUF + (wave * JA + j) * 64) * 16)));
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+      dma16(bsrc[j] + koff,
+            __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((2 * ABUF + buf * BBUF + (wave * JB + j) * 64) * 16)));
+  };
+
+  // per-lane LDS offsets (uint4 units, buffer 0) of every fragment of a step:
+  // 32x32x16 operand lane l holds row l % 32, k chunk 2 * slice + l / 32
+  const int l32 = lane & 31, lg = lane >> 5;
+  int aoff[KS][TM], boff[KS][TN];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int R = wm * TM * 32 + j * 32 + l32;
+      aoff[ks][j] = R * CPR + ((ks * 2 + lg) ^ ((R / KEYDIV) & (CPR - 1)));
+    }
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int R = wn * TN * 32 + i * 32 + l32;
+      boff[ks][i] = 2 * ABUF + R * CPR + ((ks * 2 + lg) ^ ((R / KEYDIV) & (CPR - 1)));
+    }
+  }
+
+  f16x acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // two register sets of a whole step's fragments, alternating by step parity
+  uint4 fa0[KS][TM], fb0[KS][TN], fa1[KS][TM], fb1[KS][TN];
+  auto read_frags = [&](int buf, uint4 (&fa)[KS][TM], uint4 (&fb)[KS][TN]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int i = 0; i < TN; ++i) fb[ks][i] = smem[boff[ks][i] + buf * BBUF];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) fa[ks][j] = smem[aoff[ks][j] + buf * ABUF];
+    }
+  };
+  const int nk = a.K / 64;
+  // Step kt: the fragments of kt are in (fac, fbc) and buffer kt & 1 is no
+  // longer read by this wave.  Wait for this wave's loads of step kt + 1 (the
+  // only ones in flight); after the barrier every wave's have landed and
+  // every wave holds its step-kt fragments, so buffer kt & 1 may be refilled
+  // with step kt + 2 while the MFMAs of kt run interleaved with the reads of
+  // kt + 1.  That read is unconditional (one basic block for the scheduler):
+  // past the last step it reads a stale, in-bounds buffer and is never used.
+  auto step = [&](int kt, int bcur, uint4 (&fac)[KS][TM], uint4 (&fbc)[KS][TN], uint4 (&fan)[KS][TM],
+                  uint4 (&fbn)[KS][TN]) {
+    wait_vmcnt_imm<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + 2 < nk) issue(kt + 2, bcur);
+    read_frags(bcur ^ 1, fan, fbn);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, fbc[ks][i]),
+                                                             __builtin_bit_cast(h8, fac[ks][j]), acc[i][j], 0, 0, 0);
+    // one MFMA, one LDS read, alternately; the remaining MFMAs after
+#pragma unroll
+    for (int q = 0; q < KS * (TM + TN); ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, KS * TM * TN - KS * (TM + TN), 0);
+    wait_lgkm0();
+  };
+
+  issue(0, 0);
+  if (nk > 1) {
+    issue(1, 1);
+    wait_vmcnt_imm<LPS>();
+  } else {
+    wait_vmcnt_imm<0>();
+  }
+  __builtin_amdgcn_s_barrier();
+  read_frags(0, fa0, fb0);
+  wait_lgkm0();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, 0, fa0, fb0, fa1, fb1);
+    step(kt + 1, 1, fa1, fb1, fa0, fb0);
+  }
+  if (kt < nk) step(kt, 0, fa0, fb0, fa1, fb1);
+
+  constexpr bool NT = ROLE == kGemmConv;
+  if (epilogue_staged_ok(a)) {
+    // every wave is done reading the buffers before any overwrites them
+    __builtin_amdgcn_s_barrier();
+    float* stage = reinterpret_cast<float*>(smem) + wave * 32 * (TN * 32 + 4);
+    const int m_base = m0 + wm * TM * 32, n_base = n0 + wn * TN * 32;
+    if (a.act == 1) epilogue_staged<TM, TN, 1, NT>(a, acc, stage, m_base, n_base, group);
+    else if (a.act == 2) epilogue_staged<TM, TN, 2, NT>(a, acc, stage, m_base, n_base, group);
+    else epilogue_staged<TM, TN, 0, NT>(a, acc, stage, m_base, n_base, group);
+    return;
+  }
+  const bool vec = epilogue_vec_ok(a);
+  const float* bias = a.bias ? a.bias + (int64_t)group * a.bias_group : nullptr;
+  const int64_t cg = (int64_t)group * a.c_group;
+  auto store_all = [&](auto act_tag) {
+    constexpr int ACT = decltype(act_tag)::value;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int m = m0 + wm * TM * 32 + j * 32 + l32;
+      uint64_t key = 0;
+      if (m < a.M) {
+        const int64_t rowoff = cg + c_row_offset(a, m);
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nb = n0 + wn * TN * 32 + i * 32 + 8 * q + 4 * lg;
+            if (nb < a.N) {
+              const f4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+              key = best_key4(epilogue4<half_t, ACT>(a, bias, m, rowoff, nb, v, vec), nb, a.N, key);
+            }
+          }
+        }
+      }
+      if (a.amax) {
+        // lanes l32 and l32 + 32 hold row m's columns of this wave's block
+        key = max_key_xor(key, 32);
+        if (m < a.M && lg == 0) atomicMax((unsigned long long*)(a.amax + amax_row(a, m)), (unsigned long long)key);
+      }
+    }
+  };
+  if (a.act == 1) store_all(ActTag<1>{});
+  else if (a.act == 2) store_all(ActTag<2>{});
+  else store_all(ActTag<0>{});
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int ROLE>
+hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, ROLE>), dim3(tiles, 1, a.groups), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int ROLE, int WPE>
+hipError_t launch_dlds(const GemmArgs& a, hipStream_t s) {
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_dlds_kernel<BM, BN, ROLE, WPE>), dim3(tiles, 1, a.groups), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int ROLE>
+hipError_t launch_shape(const GemmArgs& a, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    // direct-to-LDS pipeline: whole 64-wide K steps, N wide enough to fill a tile
+    if (a.K % 64 == 0 && a.N > 32) {
+      const int64_t tiles128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.groups;
+      // 128x128 tiles read less per MFMA and win on the 512-wide conv GEMMs,
+      // wherever there are at least ~400 of them, and on long-K products
+      // (FFN2, K = 3072) from ~150 of them; with fewer (N = 768 linears with
+      // short K: out-proj, projection) 128x64 tiles balance the CUs better.
+      // The thresholds were measured with the two batch halves of a forward
+      // running concurrently (half-batch FFN1 / QKV / FFN2: M = 3196).
+      if (a.N > 64 && (a.N <= 512 || tiles128 >= 400 || (a.K >= 2048 && tiles128 >= 150)))
+        return launch_dlds<128, 128, ROLE, 2>(a, s);
+      return launch_dlds<128, 64, ROLE, 3>(a, s);
+    }
+  }
+  if (a.N <= 32) return launch_t<T, 64, 32, 4, 1, ROLE>(a, s);
+  if (a.N <= 48) return launch_t<T, 128, 48, 4, 1, ROLE>(a, s);
+  if (a.N <= 64) return launch_t<T, 128, 64, 4, 1, ROLE>(a, s);
+  return launch_t<T, 128, 128, 2, 2, ROLE>(a, s);
+}
+
+}  // namespace
+
+// Launch of one GEMM role (fp16 or fp32 operands); explicitly instantiated
+// once per role in gemm_role_*.hip.
+template <int ROLE>
+hipError_t launch_gemm_role(DType t, const GemmArgs& a, hipStream_t s) {
+  return t == DType::F16 ? launch_shape<half_t, ROLE>(a, s) : launch_shape<float, ROLE>(a, s);
+}
+
+}  // namespace w2v2

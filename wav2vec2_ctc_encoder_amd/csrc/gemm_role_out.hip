@@ -1,0 +1,6 @@
+// GEMM role kGemmOut: its kernels, compiled in a translation unit of their own.
+#include "gemm_kernels.h"
+
+namespace w2v2 {
+template hipError_t launch_gemm_role<kGemmOut>(DType, const GemmArgs&, hipStream_t);
+}  // namespace w2v2

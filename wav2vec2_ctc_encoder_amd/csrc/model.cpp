@@ -220,9 +220,10 @@ struct Ws {
   float* h = nullptr;
   void *x = nullptr, *qkv = nullptr, *attn = nullptr, *ffn = nullptr, *zg = nullptr;
   float2* lnst = nullptr;  // (mean, rstd) per row of the last post-norm LayerNorm
+  uint64_t* keys = nullptr;  // per-frame argmax keys of the CTC head (w2v2_forward_greedy)
   bool shared = false;     // another part of the batch runs concurrently
 };
-constexpr int kWsRegions = 11;
+constexpr int kWsRegions = 12;
 // w2v2_forward splits a batch into up to kSplit row ranges that run
 // concurrently, one per stream (the caller's and kSplit - 1 of the model's).
 constexpr int kSplit = 2;
@@ -447,8 +448,10 @@ w2v2_status gemm_linear(w2v2_model* m, hipStream_t s, const char* name, int role
     if (st_ != W2V2_OK) return st_;     \
   } while (0)
 
+// keys: null, or the argmax slots of the B * T output frames, zero-filled,
+// which the head raises to each frame's argmax key.
 w2v2_status run_encoder(w2v2_model* m, const Ws& w, const void* feat, int B, float* logits, hipStream_t s,
-                        const Packing* pk = nullptr) {
+                        const Packing* pk = nullptr, uint64_t* keys = nullptr) {
   const w2v2_config& c = m->cfg;
   const DType dt = m->dt;
   const int T = m->Tf, d = c.hidden, F = c.ffn, G = c.pos_groups, Cg = d / G, K = c.pos_kernel;
@@ -529,8 +532,20 @@ w2v2_status run_encoder(w2v2_model* m, const Ws& w, const void* feat, int B, flo
     W2V2_LAUNCH(m, s, "layernorm",
                 launch_layernorm(dt, w.h, nullptr, M, d, m->enc_g, m->enc_b, eps, nullptr, w.x, 0, nullptr, s));
   if (!pk) {
-    W2V2_TRY(gemm_linear(m, s, "gemm_ctc_head", kGemmHead, w.x, M, c.vocab, d, m->head_w, m->head_b, 0, nullptr,
-                         logits, nullptr, c.vocab));
+    GemmArgs g;
+    g.role = kGemmHead;
+    g.A = w.x;
+    g.lda = d;
+    g.seg_rows = M;
+    g.B = m->head_w;
+    g.M = M;
+    g.N = c.vocab;
+    g.K = d;
+    g.bias = m->head_b;
+    g.out_f32 = logits;
+    g.ldc = c.vocab;
+    g.amax = keys;
+    W2V2_LAUNCH(m, s, "gemm_ctc_head", launch_gemm(dt, g, s));
     return W2V2_OK;
   }
   // packed rows -> [B, T, V] through the output row table; frames past a
@@ -548,6 +563,7 @@ w2v2_status run_encoder(w2v2_model* m, const Ws& w, const void* feat, int B, flo
   g.out_f32 = logits;
   g.ldc = c.vocab;
   g.c_rows = pk->head_rows;
+  g.amax = keys;
   W2V2_LAUNCH(m, s, "gemm_ctc_head", launch_gemm(dt, g, s));
   W2V2_LAUNCH(m, s, "zero_tail_frames", launch_zero_tail_frames(logits, B, T, c.vocab, rows.len, s));
   return W2V2_OK;
@@ -558,6 +574,141 @@ w2v2_status check_forward_args(w2v2_model* m, const void* a, const void* b, int3
   if (!a || !b || !c) return fail(W2V2_E_ARG, "a required device pointer is NULL");
   if (batch < 1 || batch > m->cfg.max_batch)
     return fail(W2V2_E_ARG, "batch must be in [1, max_batch=" + std::to_string(m->cfg.max_batch) + "]");
+  return W2V2_OK;
+}
+
+// Rows [b0, b0 + n) of every workspace region, as a workspace of its own.
+Ws ws_rows(const w2v2_model* m, int b0) {
+  auto at = [&](void* p, int i) { return (void*)((uint8_t*)p + (size_t)b0 * m->row_bytes[i]); };
+  Ws r;
+  r.bufA = at(m->w.bufA, 0);
+  r.bufB = at(m->w.bufB, 1);
+  r.gn_part = (double*)at(m->w.gn_part, 2);
+  r.gn_ss = (float2*)at(m->w.gn_ss, 3);
+  r.h = (float*)at(m->w.h, 4);
+  r.x = at(m->w.x, 5);
+  r.qkv = at(m->w.qkv, 6);
+  r.attn = at(m->w.attn, 7);
+  r.ffn = at(m->w.ffn, 8);
+  r.zg = at(m->w.zg, 9);
+  r.lnst = (float2*)at(m->w.lnst, 10);
+  r.keys = (uint64_t*)at(m->w.keys, 11);
+  return r;
+}
+
+// Whole network on rows [b0, b0 + n) of the batch, on stream s.
+// decode: the head also raises the rows' argmax keys (w.keys).
+w2v2_status forward_rows(w2v2_model* m, const float* pcm, const int32_t* valid, int b0, int n, float* logits,
+                         hipStream_t s, bool shared = false, bool decode = false) {
+  Ws w = ws_rows(m, b0);
+  w.shared = shared;
+  const void* feat = nullptr;
+  // profiling "stage": one event pair around this part's frontend and one
+  // around its encoder + head, on the part's own stream
+  const bool stage = m->prof_on && m->prof_only == "stage";
+  if (stage) m->prof->before("stage_frontend", s);
+  W2V2_TRY(run_frontend(m, w, pcm + (size_t)b0 * m->cfg.window, valid + b0, n, s, &feat));
+  if (stage) {
+    m->prof->after("stage_frontend", s);
+    m->prof->before("stage_encoder", s);
+  }
+  W2V2_TRY(run_encoder(m, w, feat, n, logits + (size_t)b0 * m->Tf * m->cfg.vocab, s, nullptr,
+                       decode ? w.keys : nullptr));
+  if (stage) m->prof->after("stage_encoder", s);
+  return W2V2_OK;
+}
+
+// One row range [b0, b0 + nb) of a true-length call on stream s: its packing
+// (device spans and starts relative to the range's own packed rows, already
+// uploaded), its row tables in the range's share of each table region, then
+// the frontend and encoder on the range's workspace slice.
+w2v2_status true_length_rows(w2v2_model* m, const float* pcm, int b0, int nb, const int64_t* P, float* logits,
+                             hipStream_t s, bool shared = false) {
+  const w2v2_config& c = m->cfg;
+  const int n = c.n_conv, Bm = c.max_batch;
+  const int32_t* dlen = m->tl_i32;
+  const int32_t* dstart = m->tl_i32 + (size_t)n * Bm;
+  const int32_t* dvalid = m->tl_i32 + (size_t)2 * n * Bm;
+  Packing pk;
+  for (int i = 0; i < n; ++i) {
+    pk.P[i] = P[i];
+    pk.lvl[i].len = dlen + (size_t)i * Bm + b0;
+    pk.lvl[i].start = dstart + (size_t)i * Bm + b0;
+  }
+  const int Tf = m->Tf, Cg = c.hidden / c.pos_groups;
+  RowTable tabs[kMaxRowTables];
+  int nt = 0, tmax = 1;
+  int64_t off = 0;  // each table region holds Bm * frames entries; this range uses rows b0 .. b0 + nb of it
+  for (int i = 1; i < n; ++i) {
+    tabs[nt] = RowTable{pk.lvl[i].start, pk.lvl[i].len, m->tl_base + (size_t)(i - 1) * Bm + b0,
+                        (int64_t)c.conv_stride[i] * c.conv_dim[i - 1], m->tl_rows + off + (int64_t)b0 * m->T[i]};
+    pk.a_rows[i] = tabs[nt].out;
+    off += (int64_t)Bm * m->T[i];
+    tmax = std::max(tmax, m->T[i]);
+    ++nt;
+  }
+  tabs[nt] = RowTable{pk.lvl[n - 1].start, pk.lvl[n - 1].len, m->tl_base + (size_t)(n - 1) * Bm + b0, Cg,
+                      m->tl_rows + off + (int64_t)b0 * Tf};
+  pk.pos_rows = tabs[nt++].out;
+  off += (int64_t)Bm * Tf;
+  tabs[nt] = RowTable{pk.lvl[n - 1].start, pk.lvl[n - 1].len, m->tl_base + (size_t)n * Bm + b0, c.vocab,
+                      m->tl_rows + off + (int64_t)b0 * Tf};
+  pk.head_rows = tabs[nt++].out;
+  tmax = std::max(tmax, Tf);
+  W2V2_LAUNCH(m, s, "row_tables", launch_row_tables(tabs, nt, nb, tmax, s));
+
+  Ws w = ws_rows(m, b0);
+  w.shared = shared;
+  const void* feat = nullptr;
+  W2V2_TRY(run_frontend(m, w, pcm + (size_t)b0 * c.window, dvalid + b0, nb, s, &feat, &pk));
+  return run_encoder(m, w, feat, nb, logits + (size_t)b0 * Tf * c.vocab, s, &pk);
+}
+
+// w2v2_forward, and with ids / lens set w2v2_forward_greedy: the head then
+// raises each frame's argmax key and the keys are collapsed into ids.
+w2v2_status forward_impl(w2v2_model* m, const float* pcm, const int32_t* valid, int32_t batch, float* logits,
+                         int32_t* vframes, int32_t* ids, int32_t* lens, void* stream) {
+  W2V2_TRY(check_forward_args(m, pcm, valid, batch, logits));
+  DeviceGuard guard(m->device);
+  hipStream_t s = (hipStream_t)stream;
+  const bool decode = ids != nullptr;
+  if (decode) W2V2_LAUNCH(m, s, "zero_keys", launch_zero_keys(m->w.keys, (int64_t)batch * m->Tf, s));
+  // profiling every kernel (no filter) runs the batch as one pass, so that each
+  // kernel's event-timed duration is its own and not shared with the other half
+  const bool serial = batch == 1 || (m->prof_on && m->prof_only.empty());
+  if (serial) {
+    W2V2_TRY(forward_rows(m, pcm, valid, 0, batch, logits, s, false, decode));
+  } else {
+    // The batch is cut into np near-equal row ranges that run concurrently,
+    // the first on the caller's stream and the others on the model's own
+    // streams, so that one part's latency-bound kernels (attention, norms,
+    // GEMM tails) overlap the other parts' work.  Rows are independent: the
+    // results are the bits of a single-stream run.
+    const int np = std::min(batch, kSplit);
+    if (hipEventRecord(m->ev_fork, s) != hipSuccess) return fail(W2V2_E_DEVICE, "fork of the streams failed");
+    for (int p = 1; p < np; ++p)
+      if (hipStreamWaitEvent(m->aux[p], m->ev_fork, 0) != hipSuccess)
+        return fail(W2V2_E_DEVICE, "fork of the streams failed");
+    w2v2_status st = W2V2_OK;
+    int b0 = 0;
+    for (int p = 0; p < np && st == W2V2_OK; ++p) {
+      const int n = batch / np + (p < batch % np ? 1 : 0);
+      st = forward_rows(m, pcm, valid, b0, n, logits, p == 0 ? s : m->aux[p], np > 1, decode);
+      b0 += n;
+    }
+    // the caller's stream waits for every part whatever happened
+    for (int p = 1; p < np; ++p)
+      if (hipEventRecord(m->ev_join[p], m->aux[p]) != hipSuccess || hipStreamWaitEvent(s, m->ev_join[p], 0) != hipSuccess)
+        return fail(W2V2_E_DEVICE, "join of the streams failed");
+    if (st != W2V2_OK) return st;
+  }
+  if (vframes)
+    W2V2_LAUNCH(m, s, "valid_frames",
+                launch_valid_frames(valid, batch, m->cfg.window, m->cfg.n_conv, m->cfg.conv_kernel,
+                                    m->cfg.conv_stride, vframes, s));
+  if (decode)
+    W2V2_LAUNCH(m, s, "ctc_collapse",
+                launch_ctc_collapse_keys(m->w.keys, vframes, batch, m->Tf, m->cfg.blank_id, ids, lens, s));
   return W2V2_OK;
 }
 
@@ -811,6 +962,7 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
       (size_t)M * F * ds,                                 // ffn
       (size_t)G * Bm * (m->Tf + K) * Cg * ds,             // zg
       (size_t)M * 8,                                      // lnst
+      (size_t)M * 8,                                      // keys
       (size_t)tl_i32_words(c) * 4 + (size_t)(c.n_conv + 1) * Bm * 8,   // true-length lengths/starts + bases
       (size_t)tl_rows_count(c, m->T, m->Tf) * 8,          // true-length row tables
   };
@@ -838,6 +990,7 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
   m->w.ffn = wsb + offs[8];
   m->w.zg = wsb + offs[9];
   m->w.lnst = (float2*)(wsb + offs[10]);
+  m->w.keys = (uint64_t*)(wsb + offs[11]);
   for (int i = 0; i < kWsRegions; ++i) m->row_bytes[i] = sizes[i] / (size_t)Bm;
   if (hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming) != hipSuccess) {
     m->ev_fork = nullptr;
@@ -856,9 +1009,9 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
       return fail(W2V2_E_DEVICE, "hipEventCreate failed");
     }
   }
-  m->tl_i32 = (int32_t*)(wsb + offs[11]);
-  m->tl_base = (int64_t*)(wsb + offs[11] + (size_t)tl_i32_words(c) * 4);
-  m->tl_rows = (int64_t*)(wsb + offs[12]);
+  m->tl_i32 = (int32_t*)(wsb + offs[12]);
+  m->tl_base = (int64_t*)(wsb + offs[12] + (size_t)tl_i32_words(c) * 4);
+  m->tl_rows = (int64_t*)(wsb + offs[13]);
   // pinned staging of the true-length tables (lengths, starts, valid, bases)
   m->tl_bytes = (size_t)tl_i32_words(c) * 4 + (size_t)(c.n_conv + 1) * Bm * 8;
   if (hipHostMalloc((void**)&m->tl_pinned, m->tl_bytes, hipHostMallocDefault) != hipSuccess) {
@@ -904,119 +1057,15 @@ w2v2_status w2v2_model_info(const w2v2_model* m, int32_t* frames_per_window, int
   return W2V2_OK;
 }
 
-// Rows [b0, b0 + n) of every workspace region, as a workspace of its own.
-Ws ws_rows(const w2v2_model* m, int b0) {
-  auto at = [&](void* p, int i) { return (void*)((uint8_t*)p + (size_t)b0 * m->row_bytes[i]); };
-  Ws r;
-  r.bufA = at(m->w.bufA, 0);
-  r.bufB = at(m->w.bufB, 1);
-  r.gn_part = (double*)at(m->w.gn_part, 2);
-  r.gn_ss = (float2*)at(m->w.gn_ss, 3);
-  r.h = (float*)at(m->w.h, 4);
-  r.x = at(m->w.x, 5);
-  r.qkv = at(m->w.qkv, 6);
-  r.attn = at(m->w.attn, 7);
-  r.ffn = at(m->w.ffn, 8);
-  r.zg = at(m->w.zg, 9);
-  r.lnst = (float2*)at(m->w.lnst, 10);
-  return r;
-}
-
-// Whole network on rows [b0, b0 + n) of the batch, on stream s.
-w2v2_status forward_rows(w2v2_model* m, const float* pcm, const int32_t* valid, int b0, int n, float* logits,
-                         hipStream_t s, bool shared = false) {
-  Ws w = ws_rows(m, b0);
-  w.shared = shared;
-  const void* feat = nullptr;
-  W2V2_TRY(run_frontend(m, w, pcm + (size_t)b0 * m->cfg.window, valid + b0, n, s, &feat));
-  return run_encoder(m, w, feat, n, logits + (size_t)b0 * m->Tf * m->cfg.vocab, s);
-}
-
 w2v2_status w2v2_forward(w2v2_model* m, const float* pcm, const int32_t* valid, int32_t batch, float* logits,
                          int32_t* vframes, void* stream) {
-  W2V2_TRY(check_forward_args(m, pcm, valid, batch, logits));
-  DeviceGuard guard(m->device);
-  hipStream_t s = (hipStream_t)stream;
-  // profiling every kernel (no filter) runs the batch as one pass, so that each
-  // kernel's event-timed duration is its own and not shared with the other half
-  const bool serial = batch == 1 || (m->prof_on && m->prof_only.empty());
-  if (serial) {
-    W2V2_TRY(forward_rows(m, pcm, valid, 0, batch, logits, s));
-  } else {
-    // The batch is cut into np near-equal row ranges that run concurrently,
-    // the first on the caller's stream and the others on the model's own
-    // streams, so that one part's latency-bound kernels (attention, norms,
-    // GEMM tails) overlap the other parts' work.  Rows are independent: the
-    // results are the bits of a single-stream run.
-    const int np = std::min(batch, kSplit);
-    if (hipEventRecord(m->ev_fork, s) != hipSuccess) return fail(W2V2_E_DEVICE, "fork of the streams failed");
-    for (int p = 1; p < np; ++p)
-      if (hipStreamWaitEvent(m->aux[p], m->ev_fork, 0) != hipSuccess)
-        return fail(W2V2_E_DEVICE, "fork of the streams failed");
-    w2v2_status st = W2V2_OK;
-    int b0 = 0;
-    for (int p = 0; p < np && st == W2V2_OK; ++p) {
-      const int n = batch / np + (p < batch % np ? 1 : 0);
-      st = forward_rows(m, pcm, valid, b0, n, logits, p == 0 ? s : m->aux[p], np > 1);
-      b0 += n;
-    }
-    // the caller's stream waits for every part whatever happened
-    for (int p = 1; p < np; ++p)
-      if (hipEventRecord(m->ev_join[p], m->aux[p]) != hipSuccess || hipStreamWaitEvent(s, m->ev_join[p], 0) != hipSuccess)
-        return fail(W2V2_E_DEVICE, "join of the streams failed");
-    if (st != W2V2_OK) return st;
-  }
-  if (vframes)
-    W2V2_LAUNCH(m, s, "valid_frames",
-                launch_valid_frames(valid, batch, m->cfg.window, m->cfg.n_conv, m->cfg.conv_kernel,
-                                    m->cfg.conv_stride, vframes, s));
-  return W2V2_OK;
+  return forward_impl(m, pcm, valid, batch, logits, vframes, nullptr, nullptr, stream);
 }
 
-// One row range [b0, b0 + nb) of a true-length call on stream s: its packing
-// (device spans and starts relative to the range's own packed rows, already
-// uploaded), its row tables in the range's share of each table region, then
-// the frontend and encoder on the range's workspace slice.
-w2v2_status true_length_rows(w2v2_model* m, const float* pcm, int b0, int nb, const int64_t* P, float* logits,
-                             hipStream_t s, bool shared = false) {
-  const w2v2_config& c = m->cfg;
-  const int n = c.n_conv, Bm = c.max_batch;
-  const int32_t* dlen = m->tl_i32;
-  const int32_t* dstart = m->tl_i32 + (size_t)n * Bm;
-  const int32_t* dvalid = m->tl_i32 + (size_t)2 * n * Bm;
-  Packing pk;
-  for (int i = 0; i < n; ++i) {
-    pk.P[i] = P[i];
-    pk.lvl[i].len = dlen + (size_t)i * Bm + b0;
-    pk.lvl[i].start = dstart + (size_t)i * Bm + b0;
-  }
-  const int Tf = m->Tf, Cg = c.hidden / c.pos_groups;
-  RowTable tabs[kMaxRowTables];
-  int nt = 0, tmax = 1;
-  int64_t off = 0;  // each table region holds Bm * frames entries; this range uses rows b0 .. b0 + nb of it
-  for (int i = 1; i < n; ++i) {
-    tabs[nt] = RowTable{pk.lvl[i].start, pk.lvl[i].len, m->tl_base + (size_t)(i - 1) * Bm + b0,
-                        (int64_t)c.conv_stride[i] * c.conv_dim[i - 1], m->tl_rows + off + (int64_t)b0 * m->T[i]};
-    pk.a_rows[i] = tabs[nt].out;
-    off += (int64_t)Bm * m->T[i];
-    tmax = std::max(tmax, m->T[i]);
-    ++nt;
-  }
-  tabs[nt] = RowTable{pk.lvl[n - 1].start, pk.lvl[n - 1].len, m->tl_base + (size_t)(n - 1) * Bm + b0, Cg,
-                      m->tl_rows + off + (int64_t)b0 * Tf};
-  pk.pos_rows = tabs[nt++].out;
-  off += (int64_t)Bm * Tf;
-  tabs[nt] = RowTable{pk.lvl[n - 1].start, pk.lvl[n - 1].len, m->tl_base + (size_t)n * Bm + b0, c.vocab,
-                      m->tl_rows + off + (int64_t)b0 * Tf};
-  pk.head_rows = tabs[nt++].out;
-  tmax = std::max(tmax, Tf);
-  W2V2_LAUNCH(m, s, "row_tables", launch_row_tables(tabs, nt, nb, tmax, s));
-
-  Ws w = ws_rows(m, b0);
-  w.shared = shared;
-  const void* feat = nullptr;
-  W2V2_TRY(run_frontend(m, w, pcm + (size_t)b0 * c.window, dvalid + b0, nb, s, &feat, &pk));
-  return run_encoder(m, w, feat, nb, logits + (size_t)b0 * Tf * c.vocab, s, &pk);
+w2v2_status w2v2_forward_greedy(w2v2_model* m, const float* pcm, const int32_t* valid, int32_t batch,
+                                float* logits, int32_t* vframes, int32_t* ids, int32_t* lens, void* stream) {
+  if (!vframes || !ids || !lens) return fail(W2V2_E_ARG, "vframes, ids and lens must not be NULL");
+  return forward_impl(m, pcm, valid, batch, logits, vframes, ids, lens, stream);
 }
 
 w2v2_status w2v2_forward_true_length(w2v2_model* m, const float* pcm, const int32_t* valid_host, int32_t batch,

@@ -85,14 +85,34 @@ def _gate_fp32(gpu, ref):
     assert err <= 1e-3, err
 
 
+def _row_mismatch_limit(n):
+    # Per-row check beside the pooled gate: at most max(2, 1% of the row's
+    # frames) mismatched frames.  A CPU emulation of this path's fp16 rounding
+    # points on the large workload puts single 799-frame rows between 99.37%
+    # and 100% (1 frame = 0.125%), the flips falling on frames whose top-2
+    # logit margin is below the fp16-mode logit error.
+    return max(2, int(np.ceil(0.01 * n)))
+
+
 def _gate_fp16(gpu, ref, vf):
+    """Pooled over the sampled rows (as the TensorRT README's quality table
+    pools its clips): Pearson >= 0.999 and argmax agreement >= 99.5%; every
+    row within _row_mismatch_limit."""
+    per = []
+    for i in range(len(vf)):
+        n = int(vf[i])
+        mis = int(np.sum(np.argmax(gpu[i, :n], -1) != np.argmax(ref[i, :n], -1)))
+        per.append((n, mis))
     sel_g = np.concatenate([gpu[i, :vf[i]] for i in range(len(vf))])
     sel_r = np.concatenate([ref[i, :vf[i]] for i in range(len(vf))])
     r = _pearson(sel_g, sel_r)
     agree = float(np.mean(np.argmax(sel_g, -1) == np.argmax(sel_r, -1)))
-    _say(f"fp16 pearson {r:.6f} argmax agreement {agree:.5f} over {len(sel_g)} frames")
+    rows = ", ".join(f"{1 - m / n if n else 1:.5f} ({m}/{n})" for n, m in per)
+    _say(f"fp16 pearson {r:.6f} argmax agreement {agree:.5f} over {len(sel_g)} frames; per row {rows}")
     assert r >= 0.999, r
     assert agree >= 0.995, agree
+    for n, m in per:
+        assert m <= _row_mismatch_limit(n), (n, m)
     return agree
 
 
@@ -289,7 +309,8 @@ def test_ctc_argmax_ties_and_large_vocab():
 # ----------------------------------------------------------------------------
 _FULL = {
     "base_10s_b1": (synth.BASE_10S_B1, (0,)),
-    "base_16s_b8": (synth.BASE_16S_B8, (0, 5)),
+    # rows 2 and 4 hold 5.6 s and 3.4 s of audio in the 16 s window
+    "base_16s_b8": (synth.BASE_16S_B8, (0, 2, 4, 5)),
     "large_16s_b4": (synth.LARGE_16S_B4, (0, 1, 2, 3)),
     "base_16s_b32": (synth.BASE_16S_B32, (0, 31)),
 }

@@ -115,7 +115,8 @@ def test_tiny_fp16_true_length_gates():
 
 # base_16s_b32: rows 0 and 31 are the first row of the first half and the
 # last row of the second half of the concurrent split
-@pytest.mark.parametrize("name,rows", [("base_16s_b8", (0, 5)), ("large_16s_b4", (1, 2)), ("base_16s_b32", (0, 31))])
+@pytest.mark.parametrize("name,rows", [("base_16s_b8", (0, 2, 4, 5)), ("large_16s_b4", (1, 2)),
+                                       ("base_16s_b32", (0, 31))])
 def test_full_workload_true_length_fp16_sampled_rows(name, rows):
     cfg = synth.PRESETS[name]
     if name == "large_16s_b4":
@@ -135,8 +136,13 @@ def test_full_workload_true_length_fp16_sampled_rows(name, rows):
     sel_r = np.concatenate([ref[i, :vf_ref[i]] for i in range(len(rows))])
     r = _pearson(sel_g, sel_r)
     agree = float(np.mean(np.argmax(sel_g, -1) == np.argmax(sel_r, -1)))
-    _say(f"fp16 pearson {r:.6f} agreement {agree:.5f} over {len(sel_g)} frames")
+    per = [(int(vf[rw]), int(np.sum(np.argmax(logits[rw, :vf[rw]], -1) != np.argmax(ref[i, :vf_ref[i]], -1))))
+           for i, rw in enumerate(rows)]
+    _say(f"fp16 pearson {r:.6f} agreement {agree:.5f} over {len(sel_g)} frames; per row (frames, mismatches) {per}")
     assert r >= 0.999 and agree >= 0.995
+    # per row: at most max(2, 1% of its frames) mismatched (see test_parity_gpu)
+    for n, m in per:
+        assert m <= max(2, int(np.ceil(0.01 * n))), (n, m)
 
 
 def test_row_bits_do_not_depend_on_the_batch():

@@ -63,6 +63,32 @@ def activation(cfg):
     return gelu_tanh if getattr(cfg, "gelu", "erf") == "tanh" else gelu
 
 
+E4M3_MAX = 448.0
+
+
+def quantize_e4m3(x: np.ndarray) -> np.ndarray:
+    """Nearest FP8 e4m3 value of x (returned as float64), ties to the even
+    mantissa, saturating at +-448.
+
+    e4m3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; the all-ones
+    exponent with mantissa 7 is NaN, so there is no infinity) holds +-2^E (1 +
+    m/8) for E = -6 .. 8 and the subnormals +-2^-6 m/8: in [2^E, 2^(E+1)) the
+    grid spacing is 2^(E-3), below 2^-6 it is 2^-9, and the largest value is
+    2^8 * 1.75 = 448.  TensorRT README, "Recipe that was measured": the FP8
+    projections quantize with per-tensor scales of amax / 448, so a value at
+    the calibrated maximum maps to 448.  Reading (the pages are silent): values
+    beyond +-448 clamp to +-448 (saturating quantization) rather than becoming
+    NaN.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(a)                        # a = f 2^e, f in [0.5, 1): floor(log2 a) = e - 1
+    E = np.clip(e - 1, -6, 8)
+    q = np.ldexp(1.0, E - 3)                  # grid spacing at a's binade (2^-9 for subnormals)
+    r = np.minimum(np.round(a / q) * q, E4M3_MAX)   # numpy rounds halves to even
+    return np.copysign(r, x)
+
+
 def layer_norm(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float,
                axis: int = -1) -> np.ndarray:
     """LayerNorm over ``axis``: biased variance, eps inside the square root."""
@@ -167,38 +193,86 @@ def softmax(s: np.ndarray, axis: int = -1) -> np.ndarray:
     return e / e.sum(axis=axis, keepdims=True)
 
 
-def self_attention(h: np.ndarray, W: dict, prefix: str, heads: int) -> np.ndarray:
+# The projections that the FP8 mode quantizes (TensorRT README, "Recipe that
+# was measured": q_proj, k_proj, v_proj, out_proj, intermediate_dense and
+# output_dense of every encoder layer), keyed by the name of the tensor their
+# input amax is stored under: q, k and v read the same input, so they share
+# one activation amax.
+FP8_INPUTS = ("attn.qkv", "attn.out", "ffn.fc1", "ffn.fc2")
+
+
+def amax_key(layer: int, which: str) -> str:
+    """Weight-table name of the calibrated input amax of projection `which`
+    (one of FP8_INPUTS) of layer `layer`."""
+    return f"layer{layer}.{which}.input_amax"
+
+
+def linear(x: np.ndarray, W: dict, name: str, s_x: float | None = None) -> np.ndarray:
+    """x W^T + b for the linear `name`.
+
+    With s_x (FP8 mode) the input and the weight pass through e4m3
+    quantize -> dequantize first, with the static per-tensor activation scale
+    s_x and the per-tensor weight scale s_w = amax(|W|) / 448 (TensorRT README,
+    "Recipe that was measured": input -> Quantize -> Dequantize -> MatMul <-
+    Dequantize <- FP8 weight).  Dequantization is taken as exact scaling, so
+    the product is (Q(x / s_x) Q(W / s_w)^T) s_x s_w.
+    """
+    dt = x.dtype
+    w = W[name + ".weight"].astype(dt)
+    if s_x is not None:
+        s_w = np.abs(w).max() / E4M3_MAX
+        x = quantize_e4m3(x / s_x) * s_x
+        w = quantize_e4m3(w / s_w) * s_w
+    return np.matmul(x, w.T) + W[name + ".bias"].astype(dt)
+
+
+def _record(record: dict | None, key: str, x: np.ndarray) -> None:
+    if record is not None:
+        record[key] = max(record.get(key, 0.0), float(np.abs(x).max()))
+
+
+def _act_scale(W: dict, fp8: bool, layer: int, which: str) -> float | None:
+    return float(np.asarray(W[amax_key(layer, which)]).reshape(-1)[0]) / E4M3_MAX if fp8 else None
+
+
+def self_attention(h: np.ndarray, W: dict, prefix: str, heads: int, fp8: bool = False,
+                   record: dict | None = None, layer: int = 0) -> np.ndarray:
     """Multi-head self-attention over all T frames, no mask.
 
     LiteRT discussion, "Rewrites for the GPU": the bidirectional mask is
     removed, so attention is plain scaled dot-product attention over the
     whole window (short clips are zero-padded).  q/k/v/out projections carry
     biases (TensorRT README, "Recipe that was measured", lists q_proj,
-    k_proj, v_proj, out_proj).  Scale 1/sqrt(d_head).
+    k_proj, v_proj, out_proj).  Scale 1/sqrt(d_head).  fp8: the four
+    projections are FP8 (see linear); the attention matmuls and softmax are
+    not.  record: receives the max |input| of the q/k/v and out projections
+    (the calibration statistic of the FP8 recipe).
     """
     bsz, t_len, d = h.shape
     dh = d // heads
     dt = h.dtype
-
-    def proj(name: str, x: np.ndarray) -> np.ndarray:
-        return np.matmul(x, W[prefix + name + ".weight"].astype(dt).T) + W[prefix + name + ".bias"].astype(dt)
-
-    q = proj("q", h).reshape(bsz, t_len, heads, dh).transpose(0, 2, 1, 3)
-    k = proj("k", h).reshape(bsz, t_len, heads, dh).transpose(0, 2, 1, 3)
-    v = proj("v", h).reshape(bsz, t_len, heads, dh).transpose(0, 2, 1, 3)
+    _record(record, amax_key(layer, "attn.qkv"), h)
+    sx = _act_scale(W, fp8, layer, "attn.qkv")
+    q = linear(h, W, prefix + "q", sx).reshape(bsz, t_len, heads, dh).transpose(0, 2, 1, 3)
+    k = linear(h, W, prefix + "k", sx).reshape(bsz, t_len, heads, dh).transpose(0, 2, 1, 3)
+    v = linear(h, W, prefix + "v", sx).reshape(bsz, t_len, heads, dh).transpose(0, 2, 1, 3)
     s = np.matmul(q, k.transpose(0, 1, 3, 2)) / np.sqrt(dt.type(dh))   # [B, H, T, T]
     o = np.matmul(softmax(s, axis=-1), v)                               # [B, H, T, dh]
     o = o.transpose(0, 2, 1, 3).reshape(bsz, t_len, d)
-    return proj("out", o)
+    _record(record, amax_key(layer, "attn.out"), o)
+    return linear(o, W, prefix + "out", _act_scale(W, fp8, layer, "attn.out"))
 
 
-def feed_forward(h: np.ndarray, W: dict, prefix: str, act=None) -> np.ndarray:
+def feed_forward(h: np.ndarray, W: dict, prefix: str, act=None, fp8: bool = False,
+                 record: dict | None = None, layer: int = 0) -> np.ndarray:
     """fc2(GELU(fc1(h))), both linears with bias (TensorRT README, "Recipe that
-    was measured": intermediate_dense and output_dense)."""
-    dt = h.dtype
+    was measured": intermediate_dense and output_dense); fp8 / record as in
+    self_attention."""
     act = gelu if act is None else act
-    u = np.matmul(h, W[prefix + "fc1.weight"].astype(dt).T) + W[prefix + "fc1.bias"].astype(dt)
-    return np.matmul(act(u), W[prefix + "fc2.weight"].astype(dt).T) + W[prefix + "fc2.bias"].astype(dt)
+    _record(record, amax_key(layer, "ffn.fc1"), h)
+    u = act(linear(h, W, prefix + "fc1", _act_scale(W, fp8, layer, "ffn.fc1")))
+    _record(record, amax_key(layer, "ffn.fc2"), u)
+    return linear(u, W, prefix + "fc2", _act_scale(W, fp8, layer, "ffn.fc2"))
 
 
 # ----------------------------------------------------------------------------
@@ -246,7 +320,7 @@ def feature_encoder(cfg, W: dict, pcm: np.ndarray, valid: np.ndarray,
     return h
 
 
-def encoder(cfg, W: dict, feats: np.ndarray) -> np.ndarray:
+def encoder(cfg, W: dict, feats: np.ndarray, fp8: bool = False, record: dict | None = None) -> np.ndarray:
     """Feature projection, positional conv and the transformer blocks.
 
     feats [B, C, T] -> hidden [B, T, d].
@@ -264,6 +338,9 @@ def encoder(cfg, W: dict, feats: np.ndarray) -> np.ndarray:
         h = LN(h);  per block: h = LN(h + MHA(h)); h = LN(h + FFN(h)).
       Stable pre-norm:
         per block: h = h + MHA(LN(h)); h = h + FFN(LN(h));  then h = LN(h).
+    * fp8: the FP8 mode of the TensorRT README's FP8 quantization study, with
+      the static activation amax of every projection input taken from the
+      weight table (amax_key); record: collects those amax values instead.
     """
     dt = feats.dtype
     eps = cfg.eps
@@ -281,15 +358,16 @@ def encoder(cfg, W: dict, feats: np.ndarray) -> np.ndarray:
         h = layer_norm(h, g("enc.norm.weight"), g("enc.norm.bias"), eps)
     for l in range(cfg.layers):
         p = f"layer{l}."
+        kw = dict(fp8=fp8, record=record, layer=l)
         if cfg.stable_layer_norm:
             a = layer_norm(h, g(p + "attn_norm.weight"), g(p + "attn_norm.bias"), eps)
-            h = h + self_attention(a, W, p + "attn.", cfg.heads)
+            h = h + self_attention(a, W, p + "attn.", cfg.heads, **kw)
             a = layer_norm(h, g(p + "ffn_norm.weight"), g(p + "ffn_norm.bias"), eps)
-            h = h + feed_forward(a, W, p + "ffn.", act)
+            h = h + feed_forward(a, W, p + "ffn.", act, **kw)
         else:
-            h = layer_norm(h + self_attention(h, W, p + "attn.", cfg.heads),
+            h = layer_norm(h + self_attention(h, W, p + "attn.", cfg.heads, **kw),
                            g(p + "attn_norm.weight"), g(p + "attn_norm.bias"), eps)
-            h = layer_norm(h + feed_forward(h, W, p + "ffn.", act),
+            h = layer_norm(h + feed_forward(h, W, p + "ffn.", act, **kw),
                            g(p + "ffn_norm.weight"), g(p + "ffn_norm.bias"), eps)
     if cfg.stable_layer_norm:
         h = layer_norm(h, g("enc.norm.weight"), g("enc.norm.bias"), eps)
@@ -309,15 +387,28 @@ def valid_frames(cfg, valid: np.ndarray) -> np.ndarray:
     return np.array([num_frames(cfg, int(v)) for v in valid], dtype=np.int32)
 
 
-def forward(cfg, W: dict, pcm: np.ndarray, valid: np.ndarray, dtype=np.float64):
+def forward(cfg, W: dict, pcm: np.ndarray, valid: np.ndarray, dtype=np.float64, fp8: bool = False):
     """Whole network: (logits [B, T, V] in ``dtype``, valid frames int32 [B]).
 
     Logits are produced for every frame of the window; only the first
-    valid-frames of each row are decoded.
+    valid-frames of each row are decoded.  fp8: the encoder projections in
+    FP8 (encoder), with the input amax entries of W.
     """
     feats = feature_encoder(cfg, W, pcm, valid, dtype)
-    h = encoder(cfg, W, feats)
+    h = encoder(cfg, W, feats, fp8=fp8)
     return ctc_head(W, h), valid_frames(cfg, valid)
+
+
+def calibrate_amax(cfg, W: dict, pcm: np.ndarray, valid: np.ndarray, dtype=np.float64) -> dict:
+    """Static activation calibration of the FP8 recipe (TensorRT README,
+    "Recipe that was measured": max(abs(input)) of every quantized projection,
+    recorded with forward pre-hooks on the float model over calibration
+    clips): runs the float network on the given windows and returns
+    {amax_key(l, which): float32 [1]} for every layer and FP8_INPUTS entry."""
+    rec: dict = {}
+    feats = feature_encoder(cfg, W, pcm, valid, dtype)
+    encoder(cfg, W, feats, record=rec)
+    return {k: np.array([v], np.float32) for k, v in rec.items()}
 
 
 def forward_true_length(cfg, W: dict, pcm: np.ndarray, valid: np.ndarray, dtype=np.float64):

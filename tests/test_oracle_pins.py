@@ -446,7 +446,7 @@ def _hf_name(n):
     return f"wav2vec2.encoder.layers.{l}.{sub[head]}.{leaf}"
 
 
-def _hf_logits(cfg, W, pcm):
+def _hf_model(cfg, W):
     torch = pytest.importorskip("torch")
     tr = pytest.importorskip("transformers")
     hc = tr.Wav2Vec2Config(
@@ -469,6 +469,12 @@ def _hf_logits(cfg, W, pcm):
     missing = set(sd) - set(new) - {"wav2vec2.masked_spec_embed"}
     assert not missing, missing
     model.load_state_dict(new, strict=False)
+    return model
+
+
+def _hf_logits(cfg, W, pcm, model=None):
+    import torch
+    model = model if model is not None else _hf_model(cfg, {k: v for k, v in W.items() if "amax" not in k})
     with torch.no_grad():
         return model(torch.from_numpy(pcm.astype(np.float64))).logits.numpy()
 
@@ -602,3 +608,164 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
     # far outside it
     assert np.abs(good - ref).max() < 1e-10
     assert np.abs(bad - ref).max() > 1e-8
+
+
+# ----------------------------------------------------------------------------
+# FP8 (e4m3) projections: quantizer, calibration, quantized network
+# ----------------------------------------------------------------------------
+def _torch_e4m3(x):
+    """torch's own float8_e4m3fn cast (round to nearest even), with the
+    saturation of the recipe applied first as a clamp."""
+    torch = pytest.importorskip("torch")
+    t = torch.from_numpy(np.clip(np.asarray(x, np.float64), -448.0, 448.0))
+    return t.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_quantize_e4m3_matches_torch_float8_cast():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(200000) * np.exp(rng.uniform(-14, 7, 200000))
+    x = x[np.abs(x) <= 448]
+    assert np.array_equal(oracle.quantize_e4m3(x), _torch_e4m3(x))
+
+
+def _ties_go_to_even(qfun):
+    """Midpoints of neighbouring e4m3 values quantize to the neighbour whose
+    code (torch's bit pattern) is even, symmetrically in sign."""
+    torch = pytest.importorskip("torch")
+    vals = torch.arange(127, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    pos = np.unique(vals)
+    mids = (pos[:-1] + pos[1:]) / 2
+    got = qfun(mids)
+    code_of = {float(v): int(c) for c, v in enumerate(vals)}
+    ok = all(g in (lo, hi) and code_of[float(g)] % 2 == 0 for lo, hi, g in zip(pos[:-1], pos[1:], got))
+    return ok and np.array_equal(qfun(-mids), -got)
+
+
+def test_quantize_e4m3_grid_ties_and_saturation():
+    torch = pytest.importorskip("torch")
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    vals = codes.to(torch.float64).numpy()
+    finite = np.isfinite(vals)
+    assert finite.sum() == 254                      # 0x7f and 0xff are NaN
+    grid = np.unique(vals[finite])
+    assert len(grid) == 253 and grid.max() == 448 and np.min(grid[grid > 0]) == 2.0 ** -9
+    # every grid value is a fixed point
+    assert np.array_equal(oracle.quantize_e4m3(grid), grid)
+    assert _ties_go_to_even(oracle.quantize_e4m3)
+    # saturation instead of NaN beyond the largest value
+    big = np.array([448.0, 449.0, 464.0, 480.0, 1e6, np.inf])
+    assert np.all(oracle.quantize_e4m3(big) == 448.0)
+    assert np.all(oracle.quantize_e4m3(-big) == -448.0)
+
+
+def _hf_amax_hooks(model, layers):
+    rec = {}
+
+    def hook(key):
+        def f(mod, args):
+            rec[key] = max(rec.get(key, 0.0), float(args[0].abs().max()))
+        return f
+    hs = []
+    for l, layer in enumerate(model.wav2vec2.encoder.layers[:layers]):
+        hs.append(layer.attention.q_proj.register_forward_pre_hook(hook(oracle.amax_key(l, "attn.qkv"))))
+        hs.append(layer.attention.out_proj.register_forward_pre_hook(hook(oracle.amax_key(l, "attn.out"))))
+        hs.append(layer.feed_forward.intermediate_dense.register_forward_pre_hook(hook(oracle.amax_key(l, "ffn.fc1"))))
+        hs.append(layer.feed_forward.output_dense.register_forward_pre_hook(hook(oracle.amax_key(l, "ffn.fc2"))))
+    return rec, hs
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("variant", ["group_postnorm", "layer_stable"])
+def test_calibrate_amax_matches_transformers_pre_hooks(variant):
+    cfg = _tiny(batch=2, **_VARIANTS[variant])
+    W = synth.make_weights(cfg)
+    pcm, valid = synth.make_pcm(cfg)
+    amax = oracle.calibrate_amax(cfg, W, pcm, valid)
+    assert sorted(amax) == sorted(oracle.amax_key(l, w) for l in range(cfg.layers) for w in oracle.FP8_INPUTS)
+    model = _hf_model(cfg, W)
+    rec, hs = _hf_amax_hooks(model, cfg.layers)
+    _hf_logits(cfg, W, pcm, model)
+    for h in hs:
+        h.remove()
+    for k, v in amax.items():
+        assert abs(float(v[0]) - np.float32(rec[k])) == 0, (k, v, rec[k])
+
+
+def _hf_fp8_logits(cfg, W, pcm):
+    """transformers' network with the FP8 recipe applied through torch: the
+    72-projection weights replaced by their e4m3 quantize-dequantize with
+    per-tensor scale amax/448, the inputs of those projections passed through
+    quantize-dequantize with the calibrated scales (forward pre-hooks)."""
+    torch = pytest.importorskip("torch")
+    model = _hf_model(cfg, {k: v for k, v in W.items() if "amax" not in k})
+    hs = []
+    for l, layer in enumerate(model.wav2vec2.encoder.layers):
+        mods = {"attn.qkv": [layer.attention.q_proj, layer.attention.k_proj, layer.attention.v_proj],
+                "attn.out": [layer.attention.out_proj], "ffn.fc1": [layer.feed_forward.intermediate_dense],
+                "ffn.fc2": [layer.feed_forward.output_dense]}
+        for which, ms in mods.items():
+            s_x = float(W[oracle.amax_key(l, which)][0]) / 448.0
+            for mod in ms:
+                w = mod.weight.data.numpy()
+                s_w = np.abs(w).max() / 448.0
+                mod.weight.data = torch.from_numpy(_torch_e4m3(w / s_w) * s_w)
+
+                def pre(m, args, s_x=s_x):
+                    return (torch.from_numpy(_torch_e4m3(args[0].numpy() / s_x) * s_x),)
+                hs.append(mod.register_forward_pre_hook(pre))
+    return _hf_logits(cfg, W, pcm, model)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("variant", ["group_postnorm", "layer_stable"])
+def test_fp8_network_matches_transformers_with_torch_fake_quant(variant):
+    cfg = _tiny(batch=2, **_VARIANTS[variant])
+    W = synth.make_weights(cfg)
+    pcm, valid = synth.make_pcm(cfg)
+    cal_pcm, cal_valid = synth.make_pcm(cfg, seed=cfg.pcm_seed + 50)
+    # half the calibrated range, so that the test inputs also saturate
+    amax = {k: v * np.float32(0.5) for k, v in oracle.calibrate_amax(cfg, W, cal_pcm, cal_valid).items()}
+    W8 = dict(W, **amax)
+    ours, _ = oracle.forward(cfg, W8, pcm, valid, fp8=True)
+    ref = _hf_fp8_logits(cfg, W8, pcm * (np.arange(cfg.window)[None, :] < valid[:, None]))
+    plain, _ = oracle.forward(cfg, W, pcm, valid)
+    assert np.abs(ours - ref).max() < 1e-9
+    # the quantization does move the logits
+    assert np.abs(ours - plain).max() > 1e-3
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("mutation", ["per_channel_weight_scale", "round_half_up", "no_saturation"])
+def test_fp8_planted_mistakes_are_caught(monkeypatch, mutation):
+    from oracle import w2v2_oracle as m
+    cfg = _tiny(batch=2)
+    W = synth.make_weights(cfg)
+    pcm, valid = synth.make_pcm(cfg)
+    cal_pcm, cal_valid = synth.make_pcm(cfg, seed=cfg.pcm_seed + 50)
+    W8 = dict(W, **{k: v * np.float32(0.5) for k, v in oracle.calibrate_amax(cfg, W, cal_pcm, cal_valid).items()})
+    q = m.quantize_e4m3
+    if mutation == "per_channel_weight_scale":
+        def lin(x, Wt, name, s_x=None):
+            w = Wt[name + ".weight"].astype(x.dtype)
+            if s_x is not None:
+                s_w = np.abs(w).max(axis=1, keepdims=True) / 448.0
+                x = q(x / s_x) * s_x
+                w = q(w / s_w) * s_w
+            return np.matmul(x, w.T) + Wt[name + ".bias"]
+        monkeypatch.setattr(m, "linear", lin)
+    elif mutation == "round_half_up":
+        # ties essentially never occur in network data: the quantizer's own
+        # tie pin is the one that catches this
+        def qu(x):
+            a = np.abs(np.asarray(x, np.float64))
+            _, e = np.frexp(a)
+            step = np.ldexp(1.0, np.clip(e - 1, -6, 8) - 3)
+            return np.copysign(np.minimum(np.floor(a / step + 0.5) * step, 448.0), x)
+        assert _ties_go_to_even(q) and not _ties_go_to_even(qu)
+        return
+    elif mutation == "no_saturation":
+        monkeypatch.setattr(m, "quantize_e4m3", lambda x: np.where(np.abs(x) > 448, np.nan, q(x)))
+    bad, _ = m.forward(cfg, W8, pcm, valid, fp8=True)
+    monkeypatch.undo()
+    ref = _hf_fp8_logits(cfg, W8, pcm * (np.arange(cfg.window)[None, :] < valid[:, None]))
+    assert not (np.abs(bad - ref).max() < 1e-9)

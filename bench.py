@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 
 METRIC = "audio-sec/sec (RTFx) + ms/window, wav2vec2-base 16 s batch 8, 1 MI355X"
 PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
@@ -156,15 +157,15 @@ def read_traffic(kernel: str, key: str = "traffic_bytes_per_launch") -> float | 
 class Workload:
     """One model with its seeded inputs and output buffers on cuda:0."""
 
-    def __init__(self, cfg, dev):
+    def __init__(self, cfg, dev, W=None, precision=None):
         import torch
 
         import synth
         import wav2vec2_ctc_encoder_amd as w2
         self.cfg = cfg
-        self.W = synth.make_weights(cfg)
+        self.W = synth.make_weights(cfg) if W is None else W
         self.pcm, self.valid = synth.make_pcm(cfg)
-        self.model = w2.Model(cfg, self.W, device=0)
+        self.model = w2.Model(cfg, self.W, device=0, precision=precision)
         B, T = cfg.batch, self.model.frames_per_window
         self.T = T
         self.tp = torch.from_numpy(self.pcm).to(dev)
@@ -271,6 +272,7 @@ def main() -> int:
     ap.add_argument("--rounds", type=int, default=7, help="interleaved rounds of the pages' timing method (0: skip)")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay rounds")
     ap.add_argument("--sweep", default="base_16s_b32", help="second workload timed beside the first ('none': skip)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-projection leg")
     ap.add_argument("--cpu-rows", type=int, default=2, help="rows the CPU oracle baseline runs (0: skip)")
     ap.add_argument("--cpu-configs", default="all", help="'all': one-row oracle baselines of every workload; 'none'")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -333,6 +335,17 @@ def main() -> int:
         r["work_unit"] = kind
         return r
 
+    # Timed region (right after the warmup): K steps of the product path (the
+    # batch halves run concurrently on two streams), bracketed by
+    # synchronizations and two events and nothing else.
+    t_wall0 = time.perf_counter()
+    ms_step = wl.timed(args.steps)
+    t_wall = time.perf_counter() - t_wall0
+    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+    window_s = cfg.window / 16000.0
+    value = B * window_s / (ms_step / 1e3)
+    valid_s = float(wl.valid.sum()) / 16000.0
+
     # Roofline pass: K steps with events around every kernel.  With every
     # kernel profiled the library runs the whole batch as one pass on one
     # stream, so each launch runs alone and its event-timed duration is the
@@ -348,17 +361,6 @@ def main() -> int:
                     "as one pass on one stream so each launch runs alone")
     print(f"[bench] roofline pass done ({ms_serial:.3f} ms/step); dominant kernel {dominant}", file=sys.stderr,
           flush=True)
-
-    # Timed region: K steps of the product path (the batch halves run
-    # concurrently on two streams), bracketed by synchronizations and two
-    # events and nothing else.
-    t_wall0 = time.perf_counter()
-    ms_step = wl.timed(args.steps)
-    t_wall = time.perf_counter() - t_wall0
-    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
-    window_s = cfg.window / 16000.0
-    value = B * window_s / (ms_step / 1e3)
-    valid_s = float(wl.valid.sum()) / 16000.0
 
     pages = wl.pages_method(args.steps, args.rounds, not args.no_graph) if args.rounds > 0 else None
     if pages:
@@ -425,6 +427,47 @@ def main() -> int:
         "ms_per_step_roofline_pass": round(ms_serial, 4),
     }
     W, pcm, valid = wl.W, wl.pcm, wl.valid
+
+    # fp8 leg: the same workload with the q/k/v/out/fc1/fc2 projections on
+    # e4m3 operands (TensorRT README, "FP8 quantization study"), calibrated
+    # by the library itself on windows of another PCM seed
+    if not args.no_fp8 and cfg.precision == "fp16" and cfg.hidden % 128 == 0 and cfg.ffn % 128 == 0:
+        cal_pcm, cal_valid = synth.make_pcm(cfg, seed=cfg.pcm_seed + 50)
+        amax = model.calibrate(torch.from_numpy(cal_pcm).to(dev), torch.from_numpy(cal_valid).to(dev))
+        torch.cuda.synchronize()
+        w8 = Workload(cfg, dev, W=dict(W, **w2.amax_table(amax)), precision="fp8")
+        for _ in range(args.warmup):
+            w8.step()
+        ms8 = w8.timed(args.steps)
+        w8.model.profile_enable(True)
+        w8.timed(args.steps)
+        pk8 = w8.model.profile_read()
+        w8.model.profile_enable(False)
+        fp8 = {"precision": "fp8 e4m3 projections (per-tensor scales, static activation calibration), "
+                            "fp16 graph otherwise",
+               "calibration": f"w2v2_calibrate of the fp16 model on {cfg.batch} windows of PCM seed "
+                              f"{cfg.pcm_seed + 50}",
+               "ms_per_step": round(ms8, 4), "audio_sec_per_sec": round(wl.audio_s / (ms8 / 1e3), 1),
+               "speedup_over_fp16": round(ms_step / ms8, 3)}
+        if args.rounds > 0:
+            fp8["pages_method_eager"] = w8.pages_method(args.steps, args.rounds, graph=False)["eager"]
+            if pages:
+                fp8["speedup_over_fp16_medians"] = round(pages["eager"]["median_ms"] /
+                                                         fp8["pages_method_eager"]["median_ms"], 3)
+        gk = {}
+        for k in ("gemm_qkv", "gemm_out_proj", "gemm_ffn1", "gemm_ffn2"):
+            if k in pk8 and k in work:
+                ms, n = pk8[k]
+                rate = work[k][1] / (ms / args.steps / 1e3) / 1e12
+                gk[k] = {"ms_per_step": round(ms / args.steps, 4), "tflops": round(rate, 1),
+                         "frac_of_fp8_peak": round(rate / PEAK_FP8_TFLOPS, 4),
+                         "fp16_ms_per_step": kernels.get(k, {}).get("ms_per_step")}
+        fp8["gemms_roofline_pass"] = gk
+        print(f"[bench] fp8 projections: {ms8:.3f} ms/step ({ms_step / ms8:.3f}x)", file=sys.stderr, flush=True)
+        out["fp8"] = fp8
+        w8.model.close()
+        del w8
+
     model.close()
     del wl
     torch.cuda.empty_cache()

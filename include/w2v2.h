@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define W2V2_ABI_VERSION 1
+#define W2V2_ABI_VERSION 2
 #define W2V2_MAX_CONV 8
 
 typedef struct w2v2_model w2v2_model; /* opaque; owned by the library */
@@ -64,7 +64,7 @@ typedef enum {
 } w2v2_status;
 
 typedef enum { W2V2_NORM_GROUP = 0, W2V2_NORM_LAYER = 1 } w2v2_feat_norm;
-typedef enum { W2V2_FP32 = 0, W2V2_FP16 = 1 } w2v2_precision;
+typedef enum { W2V2_FP32 = 0, W2V2_FP16 = 1, W2V2_FP8 = 2, W2V2_FP8_ON_FP32 = 3 } w2v2_precision;
 typedef enum { W2V2_GELU_ERF = 0, W2V2_GELU_TANH = 1 } w2v2_gelu;
 
 /*
@@ -94,6 +94,19 @@ typedef enum { W2V2_GELU_ERF = 0, W2V2_GELU_TANH = 1 } w2v2_gelu;
  *                  and matrix operands with fp32 accumulation; residual
  *                  stream, norm statistics, softmax and logits in fp32
  *                  ([TRT] "FP8 quantization study", fp16 graph).
+ *                  W2V2_FP8: the fp16 mode with the q/k/v/out/fc1/fc2
+ *                  projections of every block on FP8 e4m3 operands ([TRT]
+ *                  "FP8 quantization study", "Recipe that was measured"):
+ *                  per-tensor weight scales amax(|W|) / 448 taken at create,
+ *                  static per-tensor activation scales input_amax / 448 from
+ *                  the weight table (see w2v2_calibrate), values beyond
+ *                  +-448 saturating, fp32 accumulation, bias after the
+ *                  scaling.  Convs, feature projection, positional conv,
+ *                  norms, attention and CTC head stay as in the fp16 mode.
+ *                  W2V2_FP8_ON_FP32: the same FP8 projections with everything
+ *                  else in fp32 ([TRT] "FP8 quantization study": FP8 in the
+ *                  fp32 graph).  Both need hidden and ffn to be multiples of
+ *                  128.
  *  max_batch       largest batch a forward call may pass (workspace size).
  *  window          samples per PCM window (fixed per model, [LiteRT]
  *                  "Rewrites for the GPU").
@@ -103,7 +116,9 @@ typedef enum { W2V2_GELU_ERF = 0, W2V2_GELU_TANH = 1 } w2v2_gelu;
  *                  everywhere, for parity with graphs exported that way
  *                  ([LiteRT] "Rewrites for the GPU": GELU -> tanh-GELU).
  *
- * Supported limits (else W2V2_E_CONFIG): 1 <= n_conv <= 8, every conv_dim a
+ * Supported limits (else W2V2_E_CONFIG): sample_rate 16000 (the rate the
+ * networks of [LiteRT] "Recipe" and [TRT] intro take, with no resampling),
+ * 1 <= n_conv <= 8, every conv_dim a
  * multiple of 8 in [8, 2048] with conv_dim[0] <= 512, conv_kernel[0] <= 16,
  * conv_stride[0] <= 8, hidden and ffn multiples of 8, hidden <= 2048,
  * (hidden / pos_groups) a multiple of 8, window long enough for >= 1 frame,
@@ -111,6 +126,7 @@ typedef enum { W2V2_GELU_ERF = 0, W2V2_GELU_TANH = 1 } w2v2_gelu;
  */
 typedef struct {
   int32_t abi_version; /* must be W2V2_ABI_VERSION */
+  int32_t sample_rate; /* Hz of the PCM; must be 16000 (no resampling is done) */
   int32_t n_conv;
   int32_t conv_dim[W2V2_MAX_CONV];
   int32_t conv_kernel[W2V2_MAX_CONV];
@@ -148,6 +164,10 @@ typedef struct {
  *   layer{l}.ffn.fc1.weight [ffn, d]  .fc1.bias [ffn]  .fc2.weight [d, ffn]  .fc2.bias [d]
  *   layer{l}.ffn_norm.weight / .bias [d]
  *   head.weight [vocab, d]  head.bias [vocab]
+ * fp8 modes only, one positive value each (shape [1]): the calibrated max |x|
+ * of each quantized projection's input,
+ *   layer{l}.attn.qkv.input_amax (the input shared by q, k and v)
+ *   layer{l}.attn.out.input_amax  layer{l}.ffn.fc1.input_amax  layer{l}.ffn.fc2.input_amax
  * ndim is the number of used entries of shape (1..4).  A shape of [1,1,K]
  * is accepted for pos.weight_g.
  */
@@ -236,6 +256,23 @@ w2v2_status w2v2_forward(w2v2_model* model, const float* pcm, const int32_t* val
  */
 w2v2_status w2v2_forward_greedy(w2v2_model* model, const float* pcm, const int32_t* valid, int32_t batch,
                                 float* logits, int32_t* vframes, int32_t* ids, int32_t* lens, void* stream);
+
+/*
+ * Static activation calibration of the fp8 mode ([TRT] "Recipe that was
+ * measured": max(abs(input)) of every quantized projection, recorded on the
+ * float model over calibration clips).  Runs w2v2_forward on the batch with a
+ * W2V2_FP32 or W2V2_FP16 model and raises
+ *   amax  dev fp32 [layers][4]: slot [l][k] = max over the batch (and over
+ *         earlier calls: the caller zero-fills it once, then calls this for
+ *         each calibration batch) of |x| at the input of layer l's
+ *         k = 0 q/k/v, 1 out, 2 fc1, 3 fc2 projection.
+ * The values written to `logits` are w2v2_forward's.  The entries
+ * layer{l}.<input>.input_amax of a model in an fp8 mode are these values.
+ * Errors: W2V2_E_ARG (null model / amax, or a model in an fp8 mode), and as
+ * w2v2_forward.
+ */
+w2v2_status w2v2_calibrate(w2v2_model* model, const float* pcm, const int32_t* valid, int32_t batch,
+                           float* logits, float* amax, void* stream);
 
 /*
  * Whole network with every row taken as its own true-length clip ([TRT]

@@ -77,7 +77,7 @@ def _create(cfg_struct, weights):
     ("abi_version", 99), ("n_conv", 0), ("n_conv", 9), ("heads", 5), ("heads", 64), ("ffn", 12),
     ("pos_groups", 3), ("vocab", 0), ("blank_id", 32), ("blank_id", -1), ("eps", 0.0),
     ("precision", 7), ("max_batch", 0), ("max_batch", 5000), ("window", 399), ("feat_norm", 3),
-    ("gelu_kind", 2),
+    ("gelu_kind", 2), ("sample_rate", 8000), ("precision", 2), ("precision", 3),
 ])
 def test_bad_config_rejected_before_device_work(field, value):
     cfg, c = _config()
@@ -163,6 +163,8 @@ def test_null_arguments_rejected():
     assert lib.w2v2_forward_true_length(None, None, None, 1, None, None, None) == L.E_ARG
     assert lib.w2v2_forward_frontend(None, None, None, 1, None, None) == L.E_ARG
     assert lib.w2v2_forward_encoder(None, None, 1, None, None) == L.E_ARG
+    assert lib.w2v2_forward_greedy(None, None, None, 1, None, None, None, None, None) == L.E_ARG
+    assert lib.w2v2_calibrate(None, None, None, 1, None, None, None) == L.E_ARG
     assert lib.w2v2_ctc_greedy(None, None, 1, 10, 32, 0, None, None, None) == L.E_ARG
     # valid-looking pointers but bad sizes (no device access happens)
     p = ctypes.c_void_p(0x1000)
@@ -182,3 +184,62 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(L.LibraryMissing):
         L.lib()
+
+
+def _fp8_case(**kw):
+    """A tiny network the fp8 modes accept (hidden and ffn multiples of 128)."""
+    from wav2vec2_ctc_encoder_amd import make_config
+    cfg = synth.TINY_1S_B1.replace(hidden=128, heads=4, ffn=256, **kw)
+    W = synth.make_weights(cfg)
+    for l in range(cfg.layers):
+        for w in ("attn.qkv", "attn.out", "ffn.fc1", "ffn.fc2"):
+            W[f"layer{l}.{w}.input_amax"] = np.array([2.5], np.float32)
+    return cfg, W, make_config(cfg)
+
+
+@pytest.mark.parametrize("prec", [2, 3])
+def test_fp8_weight_table_validation(prec):
+    L = _lib()
+    cfg, W, c = _fp8_case()
+    c.precision = prec
+    # a complete table passes validation: with no GPU the call stops at the device
+    st, _, msg = _create(c, W)
+    assert st in (L.OK, L.E_DEVICE), msg
+    for case in ("missing", "zero", "negative", "shape"):
+        W2 = dict(W)
+        key = "layer1.ffn.fc2.input_amax"
+        if case == "missing":
+            W2.pop(key)
+        elif case == "zero":
+            W2[key] = np.array([0.0], np.float32)
+        elif case == "negative":
+            W2[key] = np.array([-1.0], np.float32)
+        else:
+            W2[key] = np.array([1.0, 2.0], np.float32)
+        st, _, msg = _create(c, W2)
+        assert st == L.E_WEIGHTS, (case, st, msg)
+    # the fp16 / fp32 modes take no amax entries
+    c.precision = 1
+    st, _, msg = _create(c, W)
+    assert st == L.E_WEIGHTS and "unknown weight" in msg
+
+
+def test_no_device_is_a_device_error():
+    """With a valid config and weight table and no HIP device, create fails
+    with W2V2_E_DEVICE (this container has no GPU)."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    cfg, c = _config()
+    st, h, msg = _create(c, synth.make_weights(cfg))
+    assert st == _lib().E_DEVICE, (st, msg)
+    assert h.value is None and "device" in msg.lower()
+
+
+def test_amax_table_names_match_the_oracle():
+    import oracle
+    from wav2vec2_ctc_encoder_amd import FP8_INPUTS, amax_table
+    assert tuple(FP8_INPUTS) == tuple(oracle.FP8_INPUTS)
+    t = amax_table(np.arange(8, dtype=np.float32).reshape(2, 4) + 1)
+    assert t["layer1.ffn.fc1.input_amax"][0] == 7.0
+    assert sorted(t) == sorted(oracle.amax_key(l, w) for l in range(2) for w in oracle.FP8_INPUTS)

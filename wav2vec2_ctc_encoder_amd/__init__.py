@@ -21,7 +21,18 @@ import torch
 from . import _lib
 from ._lib import W2V2Error, LibraryMissing  # noqa: F401
 
-__all__ = ["Model", "ctc_greedy", "W2V2Error", "LibraryMissing", "make_config"]
+__all__ = ["Model", "ctc_greedy", "W2V2Error", "LibraryMissing", "make_config", "amax_table", "FP8_INPUTS"]
+
+# inputs of the fp8 mode's projections, in the order of w2v2_calibrate's slots
+FP8_INPUTS = ("attn.qkv", "attn.out", "ffn.fc1", "ffn.fc2")
+
+
+def amax_table(amax) -> dict:
+    """Weight-table entries {layer{l}.<input>.input_amax: fp32 [1]} of an fp8
+    model from a calibration result [layers, 4] (tensor or array)."""
+    a = np.asarray(amax.cpu() if isinstance(amax, torch.Tensor) else amax, dtype=np.float32)
+    return {f"layer{l}.{w}.input_amax": np.array([a[l, k]], np.float32)
+            for l in range(a.shape[0]) for k, w in enumerate(FP8_INPUTS)}
 
 
 def _get(cfg: Any, name: str, default=None):
@@ -38,6 +49,7 @@ def make_config(cfg: Any, max_batch: int | None = None, precision: str | None = 
     "fp32"/"fp16", window, batch, gelu "erf"/"tanh")."""
     c = _lib.Config()
     c.abi_version = _lib.ABI_VERSION
+    c.sample_rate = int(_get(cfg, "sample_rate", 16000))
     dims, ks, ss = list(_get(cfg, "conv_dim")), list(_get(cfg, "conv_kernel")), list(_get(cfg, "conv_stride"))
     if not (len(dims) == len(ks) == len(ss)) or len(dims) > _lib.MAX_CONV:
         raise ValueError("conv_dim, conv_kernel and conv_stride must have the same length <= 8")
@@ -53,7 +65,8 @@ def make_config(cfg: Any, max_batch: int | None = None, precision: str | None = 
     c.stable_layer_norm = int(bool(_get(cfg, "stable_layer_norm", False)))
     c.eps = float(_get(cfg, "eps", 1e-5))
     prec = precision if precision is not None else _get(cfg, "precision", "fp16")
-    c.precision = {"fp32": 0, "fp16": 1}[prec] if isinstance(prec, str) else int(prec)
+    c.precision = ({"fp32": 0, "fp16": 1, "fp8": 2, "fp8_on_fp32": 3}[prec] if isinstance(prec, str)
+                   else int(prec))
     c.max_batch = int(max_batch if max_batch is not None else _get(cfg, "batch", 1))
     c.window = int(_get(cfg, "window"))
     g = _get(cfg, "gelu", "erf")
@@ -222,6 +235,23 @@ class Model:
         _lib.check(_lib.lib().w2v2_forward_encoder(self._h, _ptr(features), B, _ptr(logits), _stream(stream)),
                    "w2v2_forward_encoder")
         return logits
+
+    def calibrate(self, pcm: torch.Tensor, valid: torch.Tensor, amax: torch.Tensor | None = None,
+                  logits: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """Raise amax (cuda fp32 [layers, 4], zero-filled here if not given) to
+        the max |x| at the inputs of every block's q/k/v, out, fc1 and fc2
+        projections over this batch (``w2v2_calibrate``)."""
+        B = pcm.shape[0]
+        _need(pcm, torch.float32, (B, self.window), "pcm")
+        _need(valid, torch.int32, (B,), "valid")
+        if amax is None:
+            amax = torch.zeros(self._cfg.layers, 4, dtype=torch.float32, device=pcm.device)
+        _need(amax, torch.float32, (self._cfg.layers, 4), "amax")
+        if logits is None:
+            logits = torch.empty(B, self.frames_per_window, self.vocab, dtype=torch.float32, device=pcm.device)
+        _lib.check(_lib.lib().w2v2_calibrate(self._h, _ptr(pcm), _ptr(valid), B, _ptr(logits), _ptr(amax),
+                                             _stream(stream)), "w2v2_calibrate")
+        return amax
 
     # -- kernel timing ---------------------------------------------------
     def profile_enable(self, on: bool = True, only: str | None = None) -> None:

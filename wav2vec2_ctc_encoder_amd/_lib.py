@@ -14,7 +14,7 @@ import torch  # noqa: F401  (load torch's HIP runtime before the library)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw2v2.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 MAX_CONV = 8
 
 OK, E_ARG, E_CONFIG, E_WEIGHTS, E_NOMEM, E_DEVICE = range(6)
@@ -25,6 +25,7 @@ STATUS_NAMES = {OK: "OK", E_ARG: "E_ARG", E_CONFIG: "E_CONFIG", E_WEIGHTS: "E_WE
 class Config(ctypes.Structure):
     _fields_ = [
         ("abi_version", ctypes.c_int32),
+        ("sample_rate", ctypes.c_int32),
         ("n_conv", ctypes.c_int32),
         ("conv_dim", ctypes.c_int32 * MAX_CONV),
         ("conv_kernel", ctypes.c_int32 * MAX_CONV),
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
     L.w2v2_forward.restype = i32
     L.w2v2_forward_greedy.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp]
     L.w2v2_forward_greedy.restype = i32
+    L.w2v2_calibrate.argtypes = [vp, vp, vp, i32, vp, vp, vp]
+    L.w2v2_calibrate.restype = i32
     L.w2v2_forward_true_length.argtypes = [vp, vp, vp, i32, vp, vp, vp]
     L.w2v2_forward_true_length.restype = i32
     L.w2v2_forward_frontend.argtypes = [vp, vp, vp, i32, vp, vp]
@@ -106,7 +109,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("w2v2_create", "w2v2_destroy", "w2v2_num_frames", "w2v2_model_info", "w2v2_forward",
-            "w2v2_forward_greedy", "w2v2_forward_true_length", "w2v2_forward_frontend", "w2v2_forward_encoder",
+            "w2v2_forward_greedy", "w2v2_calibrate", "w2v2_forward_true_length", "w2v2_forward_frontend", "w2v2_forward_encoder",
             "w2v2_ctc_greedy", "w2v2_profile_enable", "w2v2_profile_read", "w2v2_last_error")
 
 

@@ -46,7 +46,8 @@ struct AttnCfg {
 
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qkv, T* __restrict__ out, int Tpad,
-                                                        RowSpan rows, int H, float c1) {
+                                                        RowSpan rows, int H, float c1, uint8_t* __restrict__ out8,
+                                                        float inv8, float* __restrict__ amax) {
   using C = AttnCfg<T, DH>;
   __shared__ uint4 sK[kKT * C::KPITCH];
   __shared__ uint4 sV[DH * C::VPITCH];
@@ -186,20 +187,25 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
   lsum = add_xor32(lsum);
   const float inv = 1.f / lsum;
   const int q = q0 + lr;
+  float vmax = 0.f;
   if (q < Tn) {
     T* orow = out + (rs + q) * dm + h * DH;
 #pragma unroll
     for (int db = 0; db < C::ND; ++db) {
       const int d0 = db * 16 + lg * 4;
-      if constexpr (sizeof(T) == 2) {
-        const h4 hv = {(half_t)(o[db][0] * inv), (half_t)(o[db][1] * inv), (half_t)(o[db][2] * inv),
-                       (half_t)(o[db][3] * inv)};
+      const float4 ov = make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+      vmax = fmaxf(vmax, fmaxf(fmaxf(fabsf(ov.x), fabsf(ov.y)), fmaxf(fabsf(ov.z), fabsf(ov.w))));
+      if (out8) {
+        *(uint32_t*)(out8 + (rs + q) * dm + h * DH + d0) = pack_e4m3x4(ov.x, ov.y, ov.z, ov.w, inv8);
+      } else if constexpr (sizeof(T) == 2) {
+        const h4 hv = {(half_t)ov.x, (half_t)ov.y, (half_t)ov.z, (half_t)ov.w};
         *(h4*)(orow + d0) = hv;
       } else {
-        *(float4*)(orow + d0) = make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+        *(float4*)(orow + d0) = ov;
       }
     }
   }
+  if (amax) wave_raise_amax(vmax, amax);
 }
 
 // ----------------------------------------------------------------------------
@@ -211,9 +217,13 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
 // 8-byte LDS writes (4 keys x 4 d per thread), exp2 is the raw hardware
 // instruction and only the last tile is masked.
 // ----------------------------------------------------------------------------
-template <int DH, int NW>
+// OUT: 0 fp16 output; 1 e4m3 output (fp8 mode); 2 fp16 output and the amax
+// of the calibration (compile-time, so the plain kernel carries neither).
+template <int DH, int NW, int OUT>
 __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restrict__ qkv, half_t* __restrict__ out,
-                                                        int Tpad, RowSpan rows, int H, float c1) {
+                                                        int Tpad, RowSpan rows, int H, float c1,
+                                                        uint8_t* __restrict__ out8, float inv8,
+                                                        float* __restrict__ amax) {
   constexpr int KT = 64;
   constexpr int KP = DH / 8 + 1;             // K row pitch (16-byte units)
   constexpr int VP = KT + 4;                 // V^T row pitch (halves)
@@ -378,15 +388,23 @@ __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restric
   lsum = add_xor32(lsum);
   const float inv = 1.f / lsum;
   const int q = qw + lr;
+  float vmax = 0.f;
   if (q < Tn) {
     half_t* orow = out + (rs + q) * dm + h * DH;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const h4 hv = {(half_t)(o[db][0] * inv), (half_t)(o[db][1] * inv), (half_t)(o[db][2] * inv),
-                     (half_t)(o[db][3] * inv)};
-      *(h4*)(orow + db * 16 + lg * 4) = hv;
+      const float4 ov = make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+      if constexpr (OUT == 2)
+        vmax = fmaxf(vmax, fmaxf(fmaxf(fabsf(ov.x), fabsf(ov.y)), fmaxf(fabsf(ov.z), fabsf(ov.w))));
+      if constexpr (OUT == 1) {
+        *(uint32_t*)(out8 + (rs + q) * dm + h * DH + db * 16 + lg * 4) = pack_e4m3x4(ov.x, ov.y, ov.z, ov.w, inv8);
+      } else {
+        const h4 hv = {(half_t)ov.x, (half_t)ov.y, (half_t)ov.z, (half_t)ov.w};
+        *(h4*)(orow + db * 16 + lg * 4) = hv;
+      }
     }
   }
+  if constexpr (OUT == 2) wave_raise_amax(vmax, amax);
 }
 
 // shared: another part of the batch runs concurrently.  The kernel then asks
@@ -395,31 +413,42 @@ __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restric
 // 128x64 GEMM workgroup) to the other part; with the GPU to itself it takes
 // up to three per CU.
 template <int DH, int NW>
-hipError_t launch_a16(const void* qkv, void* out, int B, int Tn, RowSpan rows, int H, bool shared, hipStream_t s) {
+hipError_t launch_a16(const void* qkv, void* out, int B, int Tn, RowSpan rows, int H, bool shared, hipStream_t s,
+                      uint8_t* out8, float inv8, float* amax) {
   const float c1 = 1.4426950408889634f / sqrtf((float)DH);
   constexpr size_t kStatic = 2 * 64 * (DH / 8 + 1) * 16 + 2 * DH * (64 + 4) * 2;  // sK + sV
   constexpr size_t kTwoPerCu = 56 * 1024;
   const size_t pad = (shared && kStatic < kTwoPerCu) ? kTwoPerCu - kStatic : 0;
-  hipLaunchKernelGGL((attn16_kernel<DH, NW>), dim3((Tn + NW * 16 - 1) / (NW * 16), H, B), dim3(NW * 64), pad, s,
-                     (const half_t*)qkv, (half_t*)out, Tn, rows, H, c1);
+  const dim3 grid((Tn + NW * 16 - 1) / (NW * 16), H, B);
+  if (out8)
+    hipLaunchKernelGGL((attn16_kernel<DH, NW, 1>), grid, dim3(NW * 64), pad, s, (const half_t*)qkv, (half_t*)out, Tn,
+                       rows, H, c1, out8, inv8, amax);
+  else if (amax)
+    hipLaunchKernelGGL((attn16_kernel<DH, NW, 2>), grid, dim3(NW * 64), pad, s, (const half_t*)qkv, (half_t*)out, Tn,
+                       rows, H, c1, out8, inv8, amax);
+  else
+    hipLaunchKernelGGL((attn16_kernel<DH, NW, 0>), grid, dim3(NW * 64), pad, s, (const half_t*)qkv, (half_t*)out, Tn,
+                       rows, H, c1, out8, inv8, amax);
   return hipGetLastError();
 }
 
 template <typename T, int DH>
-hipError_t launch_t(const void* qkv, void* out, int B, int Tn, RowSpan rows, int H, hipStream_t s) {
+hipError_t launch_t(const void* qkv, void* out, int B, int Tn, RowSpan rows, int H, hipStream_t s, uint8_t* out8,
+                    float inv8, float* amax) {
   const float c1 = 1.4426950408889634f / sqrtf((float)DH);  // log2(e) / sqrt(dh)
   hipLaunchKernelGGL((attention_kernel<T, DH>), dim3((Tn + kQ - 1) / kQ, H, B), dim3(256), 0, s,
-                     (const T*)qkv, (T*)out, Tn, rows, H, c1);
+                     (const T*)qkv, (T*)out, Tn, rows, H, c1, out8, inv8, amax);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_dh(const void* qkv, void* out, int B, int Tn, RowSpan rows, int H, int dh, hipStream_t s) {
+hipError_t launch_dh(const void* qkv, void* out, int B, int Tn, RowSpan rows, int H, int dh, hipStream_t s,
+                     uint8_t* out8, float inv8, float* amax) {
   switch (dh) {
-    case 16: return launch_t<T, 16>(qkv, out, B, Tn, rows, H, s);
-    case 32: return launch_t<T, 32>(qkv, out, B, Tn, rows, H, s);
-    case 64: return launch_t<T, 64>(qkv, out, B, Tn, rows, H, s);
-    case 128: return launch_t<T, 128>(qkv, out, B, Tn, rows, H, s);
+    case 16: return launch_t<T, 16>(qkv, out, B, Tn, rows, H, s, out8, inv8, amax);
+    case 32: return launch_t<T, 32>(qkv, out, B, Tn, rows, H, s, out8, inv8, amax);
+    case 64: return launch_t<T, 64>(qkv, out, B, Tn, rows, H, s, out8, inv8, amax);
+    case 128: return launch_t<T, 128>(qkv, out, B, Tn, rows, H, s, out8, inv8, amax);
     default: return hipErrorInvalidValue;
   }
 }
@@ -429,14 +458,14 @@ hipError_t launch_dh(const void* qkv, void* out, int B, int Tn, RowSpan rows, in
 bool attention_supported(int dh) { return dh == 16 || dh == 32 || dh == 64 || dh == 128; }
 
 hipError_t launch_attention(DType t, const void* qkv, void* out, int32_t B, int32_t T, RowSpan rows, int32_t H,
-                            int32_t dh, bool shared, hipStream_t s) {
+                            int32_t dh, bool shared, hipStream_t s, uint8_t* out8, float inv8, float* amax) {
   if (B <= 0 || T <= 0) return hipSuccess;
   // fp16: 16 queries per wave, 8 waves share each K/V tile
-  if (t == DType::F16 && dh == 32) return launch_a16<32, 8>(qkv, out, B, T, rows, H, shared, s);
-  if (t == DType::F16 && dh == 64) return launch_a16<64, 8>(qkv, out, B, T, rows, H, shared, s);
-  if (t == DType::F16 && dh == 128) return launch_a16<128, 8>(qkv, out, B, T, rows, H, shared, s);
-  return t == DType::F16 ? launch_dh<half_t>(qkv, out, B, T, rows, H, dh, s)
-                         : launch_dh<float>(qkv, out, B, T, rows, H, dh, s);
+  if (t == DType::F16 && dh == 32) return launch_a16<32, 8>(qkv, out, B, T, rows, H, shared, s, out8, inv8, amax);
+  if (t == DType::F16 && dh == 64) return launch_a16<64, 8>(qkv, out, B, T, rows, H, shared, s, out8, inv8, amax);
+  if (t == DType::F16 && dh == 128) return launch_a16<128, 8>(qkv, out, B, T, rows, H, shared, s, out8, inv8, amax);
+  return t == DType::F16 ? launch_dh<half_t>(qkv, out, B, T, rows, H, dh, s, out8, inv8, amax)
+                         : launch_dh<float>(qkv, out, B, T, rows, H, dh, s, out8, inv8, amax);
 }
 
 }  // namespace w2v2

@@ -9,10 +9,32 @@ namespace w2v2 {
 
 typedef _Float16 half_t;
 
-// Element type of matrix operands: fp16 in the fp16 mode, fp32 in the fp32 mode.
-enum class DType : int { F32 = 0, F16 = 1 };
+// Element type of matrix operands: fp16 in the fp16 mode, fp32 in the fp32
+// mode; F8 (e4m3) only for the encoder projections of the fp8 mode.
+enum class DType : int { F32 = 0, F16 = 1, F8 = 2 };
 
-inline size_t dsize(DType t) { return t == DType::F16 ? 2 : 4; }
+inline size_t dsize(DType t) { return t == DType::F16 ? 2 : (t == DType::F8 ? 1 : 4); }
+
+// e4m3 (OCP FP8: 1-4-3, bias 7, largest value 448) bytes of four values x * inv,
+// rounded to nearest even (v_cvt_pk_fp8_f32) after a clamp to +-448: the
+// instruction itself turns values from 480 up into NaN, the quantization of
+// the fp8 mode saturates.  Byte i holds value i.
+__device__ inline float clamp_e4m3(float x) { return fminf(fmaxf(x, -448.f), 448.f); }
+__device__ inline uint32_t pack_e4m3x4(float a, float b, float c, float d, float inv) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(a * inv), clamp_e4m3(b * inv), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(c * inv), clamp_e4m3(d * inv), w, true);
+  return (uint32_t)w;
+}
+
+// Calibration statistic: raise *amax to the largest v (>= 0) of the wave.
+// Non-negative floats order like their bit patterns, so an unsigned integer
+// maximum is the float maximum and the result does not depend on the order.
+// Every lane of the wave must call it.
+__device__ inline void wave_raise_amax(float v, float* amax) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  if ((threadIdx.x & 63) == 0) atomicMax((unsigned int*)amax, __float_as_uint(v));
+}
 
 // Exact (erf) GELU, x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), with erf from
 // Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26
@@ -153,6 +175,19 @@ struct GemmArgs {
   // after the launch it holds the row's maximum and its lowest column.  The
   // caller zero-fills amax first.
   uint64_t* amax = nullptr;
+  // fp8 mode projections (operand type F8): the accumulator of column n is
+  // scaled by col_scale[n] (activation scale times the weight scale of that
+  // column's tensor) before the bias.
+  const float* col_scale = nullptr;
+  // e4m3 operands only: out_t holds fp32 (the fp8 projections of an fp32
+  // graph) instead of fp16.
+  int32_t out_t_f32 = 0;
+  // Optional e4m3 output, laid out like out_t: e4m3(clamp(v * out_f8_inv)).
+  uint8_t* out_f8 = nullptr;
+  float out_f8_inv = 1.f;
+  // Optional calibration: *out_amax is raised to the max |v| of the values
+  // stored (see wave_raise_amax).
+  float* out_amax = nullptr;
 };
 
 // Argmax key of value v in column n: a larger value gives a larger key, and
@@ -216,9 +251,12 @@ hipError_t launch_gn0_finalize(double* part, int32_t B, int32_t k, int32_t T0, c
 // operand type (x_t); outputs fp32 (y_f32) and/or operand type (y_t); act 1
 // (erf GELU) or 2 (tanh GELU) is applied after the affine map; stats, if
 // not null, receives (mean, rstd) per row.  Input and output may alias.
+// y8 (fp8 mode): write e4m3(y * inv8) there instead of y_t; amax
+// (calibration): raised to the max |y| written.
 hipError_t launch_layernorm(DType t, const float* x_f32, const void* x_t, int64_t R, int32_t C,
                             const float* gamma, const float* beta, float eps, float* y_f32,
-                            void* y_t, int32_t act, float2* stats, hipStream_t s);
+                            void* y_t, int32_t act, float2* stats, hipStream_t s, uint8_t* y8 = nullptr,
+                            float inv8 = 1.f, float* amax = nullptr);
 // Positional-conv input: h fp32 [B, T, d] -> zg [G][B][T + K][d/G] (operand
 // type) with `pad` zero frames before the data and zeros after it.  With
 // rows set, h holds packed rows (row b's frame t at rows.start[b] + t) and
@@ -254,9 +292,12 @@ hipError_t launch_valid_frames(const int32_t* valid, int32_t B, int32_t window, 
 // rows.start[b] of qkv and out, and attends over those frames only.
 // shared: another part of the batch runs concurrently on the GPU (the fp16
 // kernel then leaves room on each CU for that part's GEMM workgroups).
+// out8 (fp8 mode): the output as e4m3(o * inv8) instead of out; amax
+// (calibration): raised to the max |o| written.
 bool attention_supported(int dh);
 hipError_t launch_attention(DType t, const void* qkv, void* out, int32_t B, int32_t T, RowSpan rows,
-                            int32_t H, int32_t dh, bool shared, hipStream_t s);
+                            int32_t H, int32_t dh, bool shared, hipStream_t s, uint8_t* out8 = nullptr,
+                            float inv8 = 1.f, float* amax = nullptr);
 
 // ----------------------------------------------------------------------------
 // CTC

@@ -117,6 +117,10 @@ __device__ inline float residual1(const GemmArgs& a, int m, int n, float r) {
 template <typename T, int ACT>
 __device__ inline f4 epilogue4(const GemmArgs& a, const float* bias, int m, int64_t rowoff, int nb, f4 v,
                                bool vec) {
+  if (a.col_scale) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] *= a.col_scale[min(nb + r, a.N - 1)];
+  }
   if (vec) {
     if (bias) {
       const float4 bb = *(const float4*)(bias + nb);
@@ -151,6 +155,14 @@ __device__ inline f4 epilogue4(const GemmArgs& a, const float* bias, int m, int6
     }
   }
   return v;
+}
+
+// Largest |v| over the valid columns nb..nb+3.
+__device__ inline float abs_max4(const f4& v, int nb, int N, float mx) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (nb + r < N) mx = fmaxf(mx, fabsf(v[r]));
+  return mx;
 }
 
 // Largest argmax key over the valid columns nb..nb+3 of one row's values.
@@ -209,7 +221,9 @@ __device__ inline bool epilogue_staged_ok(const GemmArgs& a) {
 // NT: non-temporal output stores (conv outputs: hundreds of MB written once
 // and read once by the next layer; keeping them out of the caches leaves the
 // L2 to the operand tiles).
-template <int TM, int TN, int ACT, bool NT>
+// F8: the fp8 kernel's epilogue (per-column scales, optional e4m3 output);
+// other instantiations carry neither.
+template <int TM, int TN, int ACT, bool NT, bool F8 = false>
 __device__ inline void epilogue_staged(const GemmArgs& a, f16x (&acc)[TN][TM], float* stage, int m_base,
                                        int n_base, int group) {
   constexpr int W = TN * 32;     // columns of the wave block
@@ -225,13 +239,17 @@ __device__ inline void epilogue_staged(const GemmArgs& a, f16x (&acc)[TN][TM], f
   // goes to a clamped in-bounds address without a branch, so the loads issue
   // together instead of each waiting behind the math of the previous chunk
   // (N % 8 == 0 here; values of clamped columns or rows are never stored).
-  float4 bv[TN][4];
+  float4 bv[TN][4], cv[F8 ? TN : 1][4];
+  const float* cscale = a.col_scale ? a.col_scale + (int64_t)group * a.bias_group : nullptr;
 #pragma unroll
   for (int i = 0; i < TN; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      bv[i][q] = bias ? *(const float4*)(bias + min(n_base + i * 32 + 8 * q + 4 * lg, a.N - 4))
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q = 0; q < 4; ++q) {
+      const int nc = min(n_base + i * 32 + 8 * q + 4 * lg, a.N - 4);
+      bv[i][q] = bias ? *(const float4*)(bias + nc) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (F8) cv[i][q] = cscale ? *(const float4*)(cscale + nc) : make_float4(1.f, 1.f, 1.f, 1.f);
+    }
+  float vmax = 0.f;  // calibration: max |stored value| of this lane
   const int nr = min(n_base + rcol, a.N - 8);  // the lane's 8 read-back columns
   float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0, e0 = g0, e1 = g0;
   if (a.res_stats) {
@@ -260,8 +278,16 @@ __device__ inline void epilogue_staged(const GemmArgs& a, f16x (&acc)[TN][TM], f
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int nl = i * 32 + 8 * q + 4 * lg;
-        float4 v = make_float4(acc[i][j][4 * q] + bv[i][q].x, acc[i][j][4 * q + 1] + bv[i][q].y,
-                               acc[i][j][4 * q + 2] + bv[i][q].z, acc[i][j][4 * q + 3] + bv[i][q].w);
+        float4 v;
+        if constexpr (F8) {
+          v = make_float4(fmaf(acc[i][j][4 * q], cv[i][q].x, bv[i][q].x),
+                          fmaf(acc[i][j][4 * q + 1], cv[i][q].y, bv[i][q].y),
+                          fmaf(acc[i][j][4 * q + 2], cv[i][q].z, bv[i][q].z),
+                          fmaf(acc[i][j][4 * q + 3], cv[i][q].w, bv[i][q].w));
+        } else {
+          v = make_float4(acc[i][j][4 * q] + bv[i][q].x, acc[i][j][4 * q + 1] + bv[i][q].y,
+                          acc[i][j][4 * q + 2] + bv[i][q].z, acc[i][j][4 * q + 3] + bv[i][q].w);
+        }
         v.x = act_fn<ACT>(v.x); v.y = act_fn<ACT>(v.y); v.z = act_fn<ACT>(v.z); v.w = act_fn<ACT>(v.w);
         *(float4*)(stage + l32 * P + nl) = v;
       }
@@ -299,8 +325,16 @@ __device__ inline void epilogue_staged(const GemmArgs& a, f16x (&acc)[TN][TM], f
         if (m < a.M && (lane % LPR) == 0)
           atomicMax((unsigned long long*)(a.amax + amax_row(a, m)), (unsigned long long)key);
       }
+      if (a.out_amax && m < a.M && n < a.N)
+        vmax = fmaxf(vmax, fmaxf(fmaxf(fmaxf(fabsf(x0.x), fabsf(x0.y)), fmaxf(fabsf(x0.z), fabsf(x0.w))),
+                                 fmaxf(fmaxf(fabsf(x1.x), fabsf(x1.y)), fmaxf(fabsf(x1.z), fabsf(x1.w)))));
       if (m < a.M && n < a.N) {
         const int64_t off = cg + c_row_offset(a, m) + n;
+        if (F8 && a.out_f8) {
+          const uint2 b8 = make_uint2(pack_e4m3x4(x0.x, x0.y, x0.z, x0.w, a.out_f8_inv),
+                                      pack_e4m3x4(x1.x, x1.y, x1.z, x1.w, a.out_f8_inv));
+          *(uint2*)(a.out_f8 + off) = b8;
+        }
         if (a.out_f32) {
           const f4 v0 = {x0.x, x0.y, x0.z, x0.w}, v1 = {x1.x, x1.y, x1.z, x1.w};
           if constexpr (NT) {
@@ -311,7 +345,11 @@ __device__ inline void epilogue_staged(const GemmArgs& a, f16x (&acc)[TN][TM], f
             *(f4*)(a.out_f32 + off + 4) = v1;
           }
         }
-        if (a.out_t) {
+        if (F8 && a.out_t && a.out_t_f32) {
+          const f4 v0 = {x0.x, x0.y, x0.z, x0.w}, v1 = {x1.x, x1.y, x1.z, x1.w};
+          *(f4*)((float*)a.out_t + off) = v0;
+          *(f4*)((float*)a.out_t + off + 4) = v1;
+        } else if (a.out_t) {
           const h8v hv = {(half_t)x0.x, (half_t)x0.y, (half_t)x0.z, (half_t)x0.w,
                           (half_t)x1.x, (half_t)x1.y, (half_t)x1.z, (half_t)x1.w};
           if constexpr (NT) __builtin_nontemporal_store(hv, (h8v*)((half_t*)a.out_t + off));
@@ -320,6 +358,7 @@ __device__ inline void epilogue_staged(const GemmArgs& a, f16x (&acc)[TN][TM], f
       }
     }
   }
+  if (a.out_amax) wave_raise_amax(vmax, a.out_amax);
 }
 
 template <typename T, int BM, int BN, int WM, int WN, int ROLE>
@@ -443,6 +482,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   const bool vec = epilogue_vec_ok(a);
   const float* bias = a.bias ? a.bias + (int64_t)group * a.bias_group : nullptr;
   const int64_t cg = (int64_t)group * a.c_group;
+  float vmax = 0.f;
   auto store_all = [&](auto act_tag) {
     constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
@@ -457,6 +497,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
           if (nb < a.N) {
             const f4 v = epilogue4<T, ACT>(a, bias, m, rowoff, nb, acc[i][j], vec);
             key = best_key4(v, nb, a.N, key);
+            vmax = abs_max4(v, nb, a.N, vmax);
           }
         }
       }
@@ -470,6 +511,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   if (a.act == 1) store_all(ActTag<1>{});
   else if (a.act == 2) store_all(ActTag<2>{});
   else store_all(ActTag<0>{});
+  if (a.out_amax) wave_raise_amax(vmax, a.out_amax);
 }
 
 // One wave-wide direct global->LDS load: lane l's 16 bytes at gptr land at
@@ -492,17 +534,38 @@ __device__ inline void wait_vmcnt_imm() {
 // s_waitcnt lgkmcnt(0): every LDS read of this wave has returned.
 __device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8)); }
 
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// v_mfma_scale_f32_32x32x64_f8f6f4 with both operands e4m3 and unit block
+// scales (E8M0 127 = 2^0): a 32x32 block, K = 64; lane l supplies row l % 32
+// and 32 of the 64 k values (two 16-byte chunks each for the weight and the
+// activation fragment).
+typedef int v4i __attribute__((ext_vector_type(4)));
+__device__ inline f16x mfma_f8(uint4 w0, uint4 w1, uint4 x0, uint4 x1, f16x c) {
+  const v8i wv = __builtin_shufflevector(__builtin_bit_cast(v4i, w0), __builtin_bit_cast(v4i, w1), 0, 1, 2, 3, 4, 5,
+                                         6, 7);
+  const v8i xv = __builtin_shufflevector(__builtin_bit_cast(v4i, x0), __builtin_bit_cast(v4i, x1), 0, 1, 2, 3, 4, 5,
+                                         6, 7);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, xv, c, 0, 0, 0, 127, 0, 127);
+}
+
 // WPE: waves per SIMD the register budget is fitted to (2 for 128x128 tiles,
 // 3 for 128x64, which LDS also allows: 64 / 48 KB per workgroup).
-template <int BM, int BN, int ROLE, int WPE>
+// F8: e4m3 operands (fp8 mode projections): a 128-byte tile row then holds
+// 128 k values, the step is two K = 64 MFMA slices, and each 32-row fragment
+// of a slice is two 16-byte chunks per lane (the same 4 chunk reads per
+// block and step as the fp16 kernel's four K = 16 slices).
+template <int BM, int BN, int ROLE, int WPE, bool F8 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void gemm_dlds_kernel(GemmArgs a) {
   constexpr int WM = 2, WN = 2;
   constexpr int TM = BM / WM / 32;  // 32x32 blocks per wave along m
   constexpr int TN = BN / WN / 32;  // ... along n
-  constexpr int CPR = 8;            // 16-byte chunks per tile row: 64 fp16 of K per step
+  constexpr int ES = F8 ? 1 : 2;    // operand bytes
+  constexpr int CPR = 8;            // 16-byte chunks per tile row: 128 bytes of K per step
   constexpr int RPI = 64 / CPR;     // tile rows per 1 KB wave load
   constexpr int KEYDIV = 16 / CPR;  // rows sharing a bank-group phase
-  constexpr int KS = 4;             // 16-wide K slices per step
+  constexpr int KS = F8 ? 2 : 4;    // MFMA K slices per step (64-wide fp8, 16-wide fp16)
+  constexpr int NF = 4;             // 16-byte fragment chunks per 32-row block per step
   constexpr int JA = BM / RPI / 4;  // 1 KB load instructions per wave per step (A)
   constexpr int JB = BN / RPI / 4;  // (B)
   constexpr int LPS = JA + JB;      // loads per thread per step
@@ -530,8 +593,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   const int tn = (pid % width) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  const char* Abase = (const char*)a.A + (int64_t)group * a.a_group * 2;
-  const char* Bbase = (const char*)a.B + (int64_t)group * a.b_group * 2;
+  const char* Abase = (const char*)a.A + (int64_t)group * a.a_group * ES;
+  const char* Bbase = (const char*)a.B + (int64_t)group * a.b_group * ES;
 
   // source rows (clamped) with the swizzled chunk folded in: LDS chunk p of
   // tile row r holds source chunk p ^ key(r)
@@ -541,14 +604,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   for (int j = 0; j < JA; ++j) {
     const int r = (wave * JA + j) * RPI + lane / CPR;
     const int m = min(m0 + r, a.M - 1);
-    asrc[j] = Abase + a_row_offset(a, m) * 2 + ((pos ^ ((r / KEYDIV) & (CPR - 1))) << 4);
+    asrc[j] = Abase + a_row_offset(a, m) * ES + ((pos ^ ((r / KEYDIV) & (CPR - 1))) << 4);
   }
   const char* bsrc[JB];
 #pragma unroll
   for (int j = 0; j < JB; ++j) {
     const int r = (wave * JB + j) * RPI + lane / CPR;
     const int n = min(n0 + r, a.N - 1);
-    bsrc[j] = Bbase + (int64_t)n * a.K * 2 + ((pos ^ ((r / KEYDIV) & (CPR - 1))) << 4);
+    bsrc[j] = Bbase + (int64_t)n * a.K * ES + ((pos ^ ((r / KEYDIV) & (CPR - 1))) << 4);
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)&smem[0];
   auto issue = [&](int kt, int buf) {
@@ -563,21 +626,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
             __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((2 * ABUF + buf * BBUF + (wave * JB + j) * 64) * 16)));
   };
 
-  // per-lane LDS offsets (uint4 units, buffer 0) of every fragment of a step:
-  // 32x32x16 operand lane l holds row l % 32, k chunk 2 * slice + l / 32
+  // per-lane LDS offsets (uint4 units, buffer 0) of every fragment chunk of a
+  // step: operand lane l holds row l % 32; fp16 (32x32x16): fragment f is
+  // chunk 2f + l/32; fp8 (32x32x64): slice f/2 spans chunks 4(f/2) .. +3, and
+  // lane group l/32 takes two of them (f % 2 selects which)
   const int l32 = lane & 31, lg = lane >> 5;
-  int aoff[KS][TM], boff[KS][TN];
+  int aoff[NF][TM], boff[NF][TN];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
+  for (int f = 0; f < NF; ++f) {
+    const int ch = F8 ? (4 * (f >> 1) + 2 * lg + (f & 1)) : (2 * f + lg);
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       const int R = wm * TM * 32 + j * 32 + l32;
-      aoff[ks][j] = R * CPR + ((ks * 2 + lg) ^ ((R / KEYDIV) & (CPR - 1)));
+      aoff[f][j] = R * CPR + (ch ^ ((R / KEYDIV) & (CPR - 1)));
     }
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
       const int R = wn * TN * 32 + i * 32 + l32;
-      boff[ks][i] = 2 * ABUF + R * CPR + ((ks * 2 + lg) ^ ((R / KEYDIV) & (CPR - 1)));
+      boff[f][i] = 2 * ABUF + R * CPR + (ch ^ ((R / KEYDIV) & (CPR - 1)));
     }
   }
 
@@ -590,17 +656,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   // two register sets of a whole step's fragments, alternating by step parity
-  uint4 fa0[KS][TM], fb0[KS][TN], fa1[KS][TM], fb1[KS][TN];
-  auto read_frags = [&](int buf, uint4 (&fa)[KS][TM], uint4 (&fb)[KS][TN]) {
+  uint4 fa0[NF][TM], fb0[NF][TN], fa1[NF][TM], fb1[NF][TN];
+  auto read_frags = [&](int buf, uint4 (&fa)[NF][TM], uint4 (&fb)[NF][TN]) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int f = 0; f < NF; ++f) {
 #pragma unroll
-      for (int i = 0; i < TN; ++i) fb[ks][i] = smem[boff[ks][i] + buf * BBUF];
+      for (int i = 0; i < TN; ++i) fb[f][i] = smem[boff[f][i] + buf * BBUF];
 #pragma unroll
-      for (int j = 0; j < TM; ++j) fa[ks][j] = smem[aoff[ks][j] + buf * ABUF];
+      for (int j = 0; j < TM; ++j) fa[f][j] = smem[aoff[f][j] + buf * ABUF];
     }
   };
-  const int nk = a.K / 64;
+  const int nk = a.K / (F8 ? 128 : 64);
   // Step kt: the fragments of kt are in (fac, fbc) and buffer kt & 1 is no
   // longer read by this wave.  Wait for this wave's loads of step kt + 1 (the
   // only ones in flight); after the barrier every wave's have landed and
@@ -608,27 +674,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   // with step kt + 2 while the MFMAs of kt run interleaved with the reads of
   // kt + 1.  That read is unconditional (one basic block for the scheduler):
   // past the last step it reads a stale, in-bounds buffer and is never used.
-  auto step = [&](int kt, int bcur, uint4 (&fac)[KS][TM], uint4 (&fbc)[KS][TN], uint4 (&fan)[KS][TM],
-                  uint4 (&fbn)[KS][TN]) {
+  auto step = [&](int kt, int bcur, uint4 (&fac)[NF][TM], uint4 (&fbc)[NF][TN], uint4 (&fan)[NF][TM],
+                  uint4 (&fbn)[NF][TN]) {
     wait_vmcnt_imm<0>();
     __builtin_amdgcn_s_barrier();
     if (kt + 2 < nk) issue(kt + 2, bcur);
     read_frags(bcur ^ 1, fan, fbn);
+    if constexpr (F8) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int i = 0; i < TN; ++i)
+        for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < TM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, fbc[ks][i]),
-                                                             __builtin_bit_cast(h8, fac[ks][j]), acc[i][j], 0, 0, 0);
-    // one MFMA, one LDS read, alternately; the remaining MFMAs after
+          for (int j = 0; j < TM; ++j)
+            acc[i][j] = mfma_f8(fbc[2 * ks][i], fbc[2 * ks + 1][i], fac[2 * ks][j], fac[2 * ks + 1][j], acc[i][j]);
+      // each MFMA followed by its share of the next step's LDS reads
+      constexpr int NM = KS * TM * TN, NR = NF * (TM + TN), RPM = (NR + NM - 1) / NM;
 #pragma unroll
-    for (int q = 0; q < KS * (TM + TN); ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int q = 0; q < NM; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int j = 0; j < TM; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, fbc[ks][i]),
+                                                               __builtin_bit_cast(h8, fac[ks][j]), acc[i][j], 0, 0, 0);
+      // one MFMA, one LDS read, alternately; the remaining MFMAs after
+#pragma unroll
+      for (int q = 0; q < KS * (TM + TN); ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, KS * TM * TN - KS * (TM + TN), 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, KS * TM * TN - KS * (TM + TN), 0);
     wait_lgkm0();
   };
 
@@ -655,14 +738,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     __builtin_amdgcn_s_barrier();
     float* stage = reinterpret_cast<float*>(smem) + wave * 32 * (TN * 32 + 4);
     const int m_base = m0 + wm * TM * 32, n_base = n0 + wn * TN * 32;
-    if (a.act == 1) epilogue_staged<TM, TN, 1, NT>(a, acc, stage, m_base, n_base, group);
-    else if (a.act == 2) epilogue_staged<TM, TN, 2, NT>(a, acc, stage, m_base, n_base, group);
-    else epilogue_staged<TM, TN, 0, NT>(a, acc, stage, m_base, n_base, group);
+    if (a.act == 1) epilogue_staged<TM, TN, 1, NT, F8>(a, acc, stage, m_base, n_base, group);
+    else if (a.act == 2) epilogue_staged<TM, TN, 2, NT, F8>(a, acc, stage, m_base, n_base, group);
+    else epilogue_staged<TM, TN, 0, NT, F8>(a, acc, stage, m_base, n_base, group);
     return;
   }
   const bool vec = epilogue_vec_ok(a);
   const float* bias = a.bias ? a.bias + (int64_t)group * a.bias_group : nullptr;
   const int64_t cg = (int64_t)group * a.c_group;
+  float vmax = 0.f;
   auto store_all = [&](auto act_tag) {
     constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
@@ -678,7 +762,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
             const int nb = n0 + wn * TN * 32 + i * 32 + 8 * q + 4 * lg;
             if (nb < a.N) {
               const f4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-              key = best_key4(epilogue4<half_t, ACT>(a, bias, m, rowoff, nb, v, vec), nb, a.N, key);
+              const f4 o = epilogue4<half_t, ACT>(a, bias, m, rowoff, nb, v, vec);
+              key = best_key4(o, nb, a.N, key);
+              vmax = abs_max4(o, nb, a.N, vmax);
             }
           }
         }
@@ -693,6 +779,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   if (a.act == 1) store_all(ActTag<1>{});
   else if (a.act == 2) store_all(ActTag<2>{});
   else store_all(ActTag<0>{});
+  if (a.out_amax) wave_raise_amax(vmax, a.out_amax);
 }
 
 template <typename T, int BM, int BN, int WM, int WN, int ROLE>
@@ -702,11 +789,28 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int ROLE, int WPE>
+template <int BM, int BN, int ROLE, int WPE, bool F8 = false>
 hipError_t launch_dlds(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_dlds_kernel<BM, BN, ROLE, WPE>), dim3(tiles, 1, a.groups), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_dlds_kernel<BM, BN, ROLE, WPE, F8>), dim3(tiles, 1, a.groups), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+// fp8 mode projections: e4m3 operands, whole 128-wide K steps, and the
+// staged epilogue (the only one that writes e4m3 output).
+template <int ROLE>
+hipError_t launch_f8(const GemmArgs& a, hipStream_t s) {
+  const uintptr_t ptrs = (uintptr_t)a.out_t | (uintptr_t)a.out_f32 | (uintptr_t)a.residual | (uintptr_t)a.bias |
+                         (uintptr_t)a.res_gamma | (uintptr_t)a.res_beta | (uintptr_t)a.col_scale |
+                         (uintptr_t)a.out_f8;
+  if (a.K % 128 || a.N % 8 || a.ldc % 8 || a.c_group % 8 || a.bias_group % 8 || (ptrs & 15) || a.amax)
+    return hipErrorInvalidValue;
+  const int64_t tiles128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.groups;
+  if (a.N > 64 && (tiles128 >= 400 || (a.K >= 2048 && tiles128 >= 150)))
+    return launch_dlds<128, 128, ROLE, 2, true>(a, s);
+  // the 128x64 fp8 kernel needs more than the 168 registers of three waves
+  // per SIMD (it would spill in its loop); two fit
+  return launch_dlds<128, 64, ROLE, 2, true>(a, s);
 }
 
 template <typename T, int ROLE>
@@ -738,6 +842,11 @@ hipError_t launch_shape(const GemmArgs& a, hipStream_t s) {
 // once per role in gemm_role_*.hip.
 template <int ROLE>
 hipError_t launch_gemm_role(DType t, const GemmArgs& a, hipStream_t s) {
+  if (t == DType::F8) {
+    if constexpr (ROLE == kGemmQKV || ROLE == kGemmOut || ROLE == kGemmFFN1 || ROLE == kGemmFFN2)
+      return launch_f8<ROLE>(a, s);
+    return hipErrorInvalidValue;
+  }
   return t == DType::F16 ? launch_shape<half_t, ROLE>(a, s) : launch_shape<float, ROLE>(a, s);
 }
 

@@ -68,6 +68,10 @@ struct DeviceGuard {
 
 int conv_len(int64_t n, int k, int s) { return n < k ? 0 : (int)((n - k) / s + 1); }
 
+// Inputs of the fp8 mode's projections, in the order of their calibration
+// slots: q/k/v (one shared input), out, fc1, fc2.
+const char* const kFp8Inputs[4] = {"attn.qkv", "attn.out", "ffn.fc1", "ffn.fc2"};
+
 struct ExpectedW {
   std::string name;
   std::vector<int64_t> shape;
@@ -110,6 +114,8 @@ std::vector<ExpectedW> expected_weights(const w2v2_config& c) {
     out.push_back({p + "ffn.fc2.bias", {d}});
     out.push_back({p + "ffn_norm.weight", {d}});
     out.push_back({p + "ffn_norm.bias", {d}});
+    if (c.precision == W2V2_FP8 || c.precision == W2V2_FP8_ON_FP32)
+      for (const char* w : kFp8Inputs) out.push_back({p + w + ".input_amax", {1}});
   }
   out.push_back({"head.weight", {c.vocab, d}});
   out.push_back({"head.bias", {c.vocab}});
@@ -119,6 +125,7 @@ std::vector<ExpectedW> expected_weights(const w2v2_config& c) {
 std::string check_config(const w2v2_config& c, int* frames_out) {
   auto bad = [](const char* m) { return std::string(m); };
   if (c.abi_version != W2V2_ABI_VERSION) return bad("abi_version does not match W2V2_ABI_VERSION");
+  if (c.sample_rate != 16000) return bad("sample_rate must be 16000 (PCM is not resampled)");
   if (c.n_conv < 1 || c.n_conv > W2V2_MAX_CONV) return bad("n_conv must be in [1, 8]");
   for (int i = 0; i < c.n_conv; ++i) {
     if (c.conv_dim[i] < 8 || c.conv_dim[i] > 2048 || c.conv_dim[i] % 8)
@@ -142,7 +149,12 @@ std::string check_config(const w2v2_config& c, int* frames_out) {
   if (c.vocab < 1) return bad("vocab must be >= 1");
   if (c.blank_id < 0 || c.blank_id >= c.vocab) return bad("blank_id must be in [0, vocab)");
   if (!(c.eps > 0.f) || !std::isfinite(c.eps)) return bad("eps must be positive and finite");
-  if (c.precision != W2V2_FP32 && c.precision != W2V2_FP16) return bad("unknown precision");
+  if (c.precision != W2V2_FP32 && c.precision != W2V2_FP16 && c.precision != W2V2_FP8 &&
+      c.precision != W2V2_FP8_ON_FP32)
+    return bad("unknown precision");
+  const bool fp8 = c.precision == W2V2_FP8 || c.precision == W2V2_FP8_ON_FP32;
+  if (fp8 && (c.hidden % 128 || c.ffn % 128))
+    return bad("the fp8 mode needs hidden and ffn to be multiples of 128");
   if (c.gelu_kind != W2V2_GELU_ERF && c.gelu_kind != W2V2_GELU_TANH) return bad("unknown gelu_kind");
   if (c.max_batch < 1 || c.max_batch > 4096) return bad("max_batch must be in [1, 4096]");
   if (c.window < 1) return bad("window must be >= 1");
@@ -257,6 +269,11 @@ struct w2v2_model {
     const void *wqkv = nullptr, *wo = nullptr, *w1 = nullptr, *w2 = nullptr;
     const float *bqkv = nullptr, *bo = nullptr, *b1 = nullptr, *b2 = nullptr;
     const float *ln1_g = nullptr, *ln1_b = nullptr, *ln2_g = nullptr, *ln2_b = nullptr;
+    // fp8 mode: per-column accumulator scales (activation scale x weight
+    // scale) of the qkv / out / fc1 / fc2 GEMMs and the inverse activation
+    // scales 448 / amax of their inputs, in that order
+    const float* cs[4] = {};
+    float inv[4] = {1.f, 1.f, 1.f, 1.f};
   };
   std::vector<Layer> layers;
   const void* head_w = nullptr;
@@ -283,6 +300,8 @@ struct w2v2_model {
 
   Profiler* prof = nullptr;
   bool prof_on = false;
+  bool fp8 = false;           // fp8 mode: e4m3 encoder projections
+  float* calib = nullptr;     // during w2v2_calibrate: [layers][4] amax slots
   std::string prof_only;  // empty: every kernel
 
   ~w2v2_model() {
@@ -312,6 +331,57 @@ struct Arena {
 };
 
 size_t add_f32(Arena& a, const std::vector<float>& v) { return a.add(v.data(), v.size() * 4); }
+
+// e4m3 (OCP FP8: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits) code
+// of v: the nearest of +-2^E (1 + m/8), E = -6 .. 8 (448 the largest), and
+// the subnormals +-2^-6 m/8, ties to the even mantissa; larger magnitudes
+// saturate to 448.  Weights are quantized with it at create.
+uint8_t e4m3_code(double v) {
+  const uint8_t sign = std::signbit(v) ? 0x80 : 0;
+  const double a = std::fabs(v);
+  if (!(a == a)) return 0x7F;
+  if (a >= 448.0) return sign | 0x7E;
+  int e = 0;
+  std::frexp(a, &e);                                 // a = f 2^e, f in [0.5, 1)
+  int E = std::max(e - 1, -6);
+  const double q = std::ldexp(1.0, E - 3);           // grid spacing of a's binade
+  const double r = std::nearbyint(a / q) * q;        // round to nearest, ties to even
+  if (r >= 448.0) return sign | 0x7E;
+  if (r == 0.0) return sign;
+  std::frexp(r, &e);
+  E = e - 1;
+  if (E < -6) return sign | (uint8_t)std::lrint(r / std::ldexp(1.0, -9));   // subnormal: m = r / 2^-9
+  const int mant = (int)std::lrint((r / std::ldexp(1.0, E) - 1.0) * 8.0);
+  return sign | (uint8_t)(((E + 7) << 3) | mant);
+}
+
+double amax_of(const float* p, size_t n) {
+  double mx = 0.0;
+  for (size_t i = 0; i < n; ++i) mx = std::max(mx, (double)std::fabs(p[i]));
+  return mx;
+}
+
+// v as e4m3 codes, consecutive blocks of `block` values with their own scales
+// (the per-tensor weight scales amax / 448; a zero tensor keeps scale 0 and
+// codes 0)
+size_t add_e4m3(Arena& a, const std::vector<float>& v, const std::vector<double>& scale, size_t block) {
+  std::vector<uint8_t> q(v.size());
+  for (size_t i = 0; i < v.size(); ++i) {
+    const double sc = scale[i / block];
+    q[i] = sc > 0.0 ? e4m3_code((double)v[i] / sc) : 0;
+  }
+  return a.add(q.data(), q.size());
+}
+
+
+// one fp8 linear [N, K]: the e4m3 weight and its per-column accumulator
+// scales (input amax / 448) x (weight amax / 448)
+size_t add_fp8_linear(Arena& a, const std::vector<float>& w, double in_amax, int N, size_t* cs_off) {
+  const double sw = amax_of(w.data(), w.size()) / 448.0;
+  const size_t off = add_e4m3(a, w, {sw}, w.size());
+  *cs_off = add_f32(a, std::vector<float>((size_t)N, (float)(in_amax / 448.0 * sw)));
+  return off;
+}
 
 size_t add_t(Arena& a, DType dt, const std::vector<float>& v) {
   if (dt == DType::F32) return add_f32(a, v);
@@ -414,9 +484,20 @@ struct ResNorm {
   const float *gamma, *beta;
 };
 
+// Operands and outputs of an encoder projection beyond the defaults: in the
+// fp8 mode e4m3 operands with per-column accumulator scales and optionally
+// e4m3 output; during calibration the amax slot of the output.
+struct ProjIO {
+  bool f8 = false;
+  const float* col_scale = nullptr;
+  uint8_t* out8 = nullptr;
+  float out8_inv = 1.f;
+  float* out_amax = nullptr;
+};
+
 w2v2_status gemm_linear(w2v2_model* m, hipStream_t s, const char* name, int role, const void* A, int M, int N,
                         int K, const void* W, const float* bias, int act, const float* residual, float* out32,
-                        void* outt, int64_t ldc, const ResNorm* rn = nullptr) {
+                        void* outt, int64_t ldc, const ResNorm* rn = nullptr, const ProjIO& io = ProjIO()) {
   GemmArgs g;
   g.role = role;
   g.A = A;
@@ -436,9 +517,14 @@ w2v2_status gemm_linear(w2v2_model* m, hipStream_t s, const char* name, int role
     g.res_beta = rn->beta;
   }
   g.out_f32 = out32;
-  g.out_t = outt;
+  g.out_t = io.out8 ? nullptr : outt;
   g.ldc = ldc;
-  W2V2_LAUNCH(m, s, name, launch_gemm(m->dt, g, s));
+  g.col_scale = io.col_scale;
+  g.out_t_f32 = io.f8 && m->dt == DType::F32;
+  g.out_f8 = io.out8;
+  g.out_f8_inv = io.out8_inv;
+  g.out_amax = io.out_amax;
+  W2V2_LAUNCH(m, s, name, launch_gemm(io.f8 ? DType::F8 : m->dt, g, s));
   return W2V2_OK;
 }
 
@@ -496,41 +582,63 @@ w2v2_status run_encoder(w2v2_model* m, const Ws& w, const void* feat, int B, flo
   // statistics; the raw residual sum stays in h, and the next residual GEMM
   // (out-proj, FFN2) applies that LayerNorm to h as it reads it.
   // Stable pre-norm: the LayerNorms feed x only and h is the plain sum.
+  // fp8 mode: the operands of the four projections of every block (x for
+  // qkv and fc1, the attention output, the FFN hidden) are written as e4m3
+  // with their input's static scale, and those GEMMs run on e4m3 operands;
+  // the CTC head keeps fp16 operands.  Calibration (m->calib): the producers
+  // of those operands raise their input's amax slot instead.
   const bool stable = c.stable_layer_norm != 0;
+  const bool f8 = m->fp8;
+  auto slot = [&](int l, int k) { return m->calib ? m->calib + 4 * l + k : nullptr; };
+  // LayerNorm of h into x for projection k (0 qkv, 2 fc1) of layer l; l equal
+  // to the layer count means the CTC head
+  auto ln_to_x = [&](const float* g, const float* b, float2* stats, int l, int k) {
+    const bool proj = l < c.layers;
+    uint8_t* y8 = (f8 && proj) ? (uint8_t*)w.x : nullptr;
+    return launch_layernorm(dt, w.h, nullptr, M, d, g, b, eps, nullptr, y8 ? nullptr : w.x, 0, stats, s, y8,
+                            y8 ? m->layers[l].inv[k] : 1.f, proj ? slot(l, k) : nullptr);
+  };
   ResNorm rn{w.lnst, m->enc_g, m->enc_b};
-  if (!stable)
-    W2V2_LAUNCH(m, s, "layernorm",
-                launch_layernorm(dt, w.h, nullptr, M, d, m->enc_g, m->enc_b, eps, nullptr, w.x, 0, w.lnst, s));
+  if (!stable) W2V2_LAUNCH(m, s, "layernorm", ln_to_x(m->enc_g, m->enc_b, w.lnst, 0, 0));
 
   for (int l = 0; l < c.layers; ++l) {
     const w2v2_model::Layer& L = m->layers[l];
-    if (stable)
-      W2V2_LAUNCH(m, s, "layernorm",
-                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, nullptr, w.x, 0, nullptr, s));
-    W2V2_TRY(gemm_linear(m, s, "gemm_qkv", kGemmQKV, w.x, M, 3 * d, d, L.wqkv, L.bqkv, 0, nullptr, nullptr, w.qkv, 3 * d));
-    W2V2_LAUNCH(m, s, "attention", launch_attention(dt, w.qkv, w.attn, B, T, rows, c.heads, d / c.heads, w.shared, s));
+    auto io = [&](int k) {
+      ProjIO r;
+      r.f8 = f8;
+      r.col_scale = f8 ? L.cs[k] : nullptr;
+      return r;
+    };
+    if (stable) W2V2_LAUNCH(m, s, "layernorm", ln_to_x(L.ln1_g, L.ln1_b, nullptr, l, 0));
+    W2V2_TRY(gemm_linear(m, s, "gemm_qkv", kGemmQKV, w.x, M, 3 * d, d, L.wqkv, L.bqkv, 0, nullptr, nullptr, w.qkv,
+                         3 * d, nullptr, io(0)));
+    W2V2_LAUNCH(m, s, "attention",
+                launch_attention(dt, w.qkv, w.attn, B, T, rows, c.heads, d / c.heads, w.shared, s,
+                                 f8 ? (uint8_t*)w.attn : nullptr, L.inv[1], slot(l, 1)));
     W2V2_TRY(gemm_linear(m, s, "gemm_out_proj", kGemmOut, w.attn, M, d, d, L.wo, L.bo, 0, w.h, w.h, nullptr, d,
-                         stable ? nullptr : &rn));
+                         stable ? nullptr : &rn, io(1)));
     if (stable) {
-      W2V2_LAUNCH(m, s, "layernorm",
-                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln2_g, L.ln2_b, eps, nullptr, w.x, 0, nullptr, s));
+      W2V2_LAUNCH(m, s, "layernorm", ln_to_x(L.ln2_g, L.ln2_b, nullptr, l, 2));
     } else {
-      W2V2_LAUNCH(m, s, "layernorm",
-                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln1_g, L.ln1_b, eps, nullptr, w.x, 0, w.lnst, s));
+      W2V2_LAUNCH(m, s, "layernorm", ln_to_x(L.ln1_g, L.ln1_b, w.lnst, l, 2));
       rn = ResNorm{w.lnst, L.ln1_g, L.ln1_b};
     }
-    W2V2_TRY(gemm_linear(m, s, "gemm_ffn1", kGemmFFN1, w.x, M, F, d, L.w1, L.b1, m->act, nullptr, nullptr, w.ffn, F));
+    ProjIO io1 = io(2);
+    if (f8) {
+      io1.out8 = (uint8_t*)w.ffn;
+      io1.out8_inv = L.inv[3];
+    }
+    io1.out_amax = slot(l, 3);
+    W2V2_TRY(gemm_linear(m, s, "gemm_ffn1", kGemmFFN1, w.x, M, F, d, L.w1, L.b1, m->act, nullptr, nullptr, w.ffn, F,
+                         nullptr, io1));
     W2V2_TRY(gemm_linear(m, s, "gemm_ffn2", kGemmFFN2, w.ffn, M, d, F, L.w2, L.b2, 0, w.h, w.h, nullptr, d,
-                         stable ? nullptr : &rn));
+                         stable ? nullptr : &rn, io(3)));
     if (!stable) {
-      W2V2_LAUNCH(m, s, "layernorm",
-                  launch_layernorm(dt, w.h, nullptr, M, d, L.ln2_g, L.ln2_b, eps, nullptr, w.x, 0, w.lnst, s));
+      W2V2_LAUNCH(m, s, "layernorm", ln_to_x(L.ln2_g, L.ln2_b, w.lnst, l + 1, 0));
       rn = ResNorm{w.lnst, L.ln2_g, L.ln2_b};
     }
   }
-  if (stable)
-    W2V2_LAUNCH(m, s, "layernorm",
-                launch_layernorm(dt, w.h, nullptr, M, d, m->enc_g, m->enc_b, eps, nullptr, w.x, 0, nullptr, s));
+  if (stable) W2V2_LAUNCH(m, s, "layernorm", ln_to_x(m->enc_g, m->enc_b, nullptr, c.layers, 0));
   if (!pk) {
     GemmArgs g;
     g.role = kGemmHead;
@@ -578,29 +686,31 @@ w2v2_status check_forward_args(w2v2_model* m, const void* a, const void* b, int3
 }
 
 // Rows [b0, b0 + n) of every workspace region, as a workspace of its own.
-Ws ws_rows(const w2v2_model* m, int b0) {
+// base: the whole-batch regions (the model's workspace).
+Ws ws_rows(const w2v2_model* m, const Ws& base, int b0) {
   auto at = [&](void* p, int i) { return (void*)((uint8_t*)p + (size_t)b0 * m->row_bytes[i]); };
   Ws r;
-  r.bufA = at(m->w.bufA, 0);
-  r.bufB = at(m->w.bufB, 1);
-  r.gn_part = (double*)at(m->w.gn_part, 2);
-  r.gn_ss = (float2*)at(m->w.gn_ss, 3);
-  r.h = (float*)at(m->w.h, 4);
-  r.x = at(m->w.x, 5);
-  r.qkv = at(m->w.qkv, 6);
-  r.attn = at(m->w.attn, 7);
-  r.ffn = at(m->w.ffn, 8);
-  r.zg = at(m->w.zg, 9);
-  r.lnst = (float2*)at(m->w.lnst, 10);
-  r.keys = (uint64_t*)at(m->w.keys, 11);
+  r.bufA = at(base.bufA, 0);
+  r.bufB = at(base.bufB, 1);
+  r.gn_part = (double*)at(base.gn_part, 2);
+  r.gn_ss = (float2*)at(base.gn_ss, 3);
+  r.h = (float*)at(base.h, 4);
+  r.x = at(base.x, 5);
+  r.qkv = at(base.qkv, 6);
+  r.attn = at(base.attn, 7);
+  r.ffn = at(base.ffn, 8);
+  r.zg = at(base.zg, 9);
+  r.lnst = (float2*)at(base.lnst, 10);
+  r.keys = (uint64_t*)at(base.keys, 11);
   return r;
 }
+Ws ws_rows(const w2v2_model* m, int b0) { return ws_rows(m, m->w, b0); }
 
 // Whole network on rows [b0, b0 + n) of the batch, on stream s.
 // decode: the head also raises the rows' argmax keys (w.keys).
-w2v2_status forward_rows(w2v2_model* m, const float* pcm, const int32_t* valid, int b0, int n, float* logits,
-                         hipStream_t s, bool shared = false, bool decode = false) {
-  Ws w = ws_rows(m, b0);
+w2v2_status forward_rows(w2v2_model* m, const Ws& base, const float* pcm, const int32_t* valid, int b0, int n,
+                         float* logits, hipStream_t s, bool shared = false, bool decode = false) {
+  Ws w = ws_rows(m, base, b0);
   w.shared = shared;
   const void* feat = nullptr;
   // profiling "stage": one event pair around this part's frontend and one
@@ -666,18 +776,20 @@ w2v2_status true_length_rows(w2v2_model* m, const float* pcm, int b0, int nb, co
 
 // w2v2_forward, and with ids / lens set w2v2_forward_greedy: the head then
 // raises each frame's argmax key and the keys are collapsed into ids.
+// ws: the whole-batch workspace regions (null: the model's).
 w2v2_status forward_impl(w2v2_model* m, const float* pcm, const int32_t* valid, int32_t batch, float* logits,
-                         int32_t* vframes, int32_t* ids, int32_t* lens, void* stream) {
+                         int32_t* vframes, int32_t* ids, int32_t* lens, void* stream, const Ws* ws = nullptr) {
   W2V2_TRY(check_forward_args(m, pcm, valid, batch, logits));
   DeviceGuard guard(m->device);
   hipStream_t s = (hipStream_t)stream;
+  const Ws& base = ws ? *ws : m->w;
   const bool decode = ids != nullptr;
-  if (decode) W2V2_LAUNCH(m, s, "zero_keys", launch_zero_keys(m->w.keys, (int64_t)batch * m->Tf, s));
+  if (decode) W2V2_LAUNCH(m, s, "zero_keys", launch_zero_keys(base.keys, (int64_t)batch * m->Tf, s));
   // profiling every kernel (no filter) runs the batch as one pass, so that each
   // kernel's event-timed duration is its own and not shared with the other half
   const bool serial = batch == 1 || (m->prof_on && m->prof_only.empty());
   if (serial) {
-    W2V2_TRY(forward_rows(m, pcm, valid, 0, batch, logits, s, false, decode));
+    W2V2_TRY(forward_rows(m, base, pcm, valid, 0, batch, logits, s, false, decode));
   } else {
     // The batch is cut into np near-equal row ranges that run concurrently,
     // the first on the caller's stream and the others on the model's own
@@ -693,7 +805,7 @@ w2v2_status forward_impl(w2v2_model* m, const float* pcm, const int32_t* valid, 
     int b0 = 0;
     for (int p = 0; p < np && st == W2V2_OK; ++p) {
       const int n = batch / np + (p < batch % np ? 1 : 0);
-      st = forward_rows(m, pcm, valid, b0, n, logits, p == 0 ? s : m->aux[p], np > 1, decode);
+      st = forward_rows(m, base, pcm, valid, b0, n, logits, p == 0 ? s : m->aux[p], np > 1, decode);
       b0 += n;
     }
     // the caller's stream waits for every part whatever happened
@@ -708,7 +820,7 @@ w2v2_status forward_impl(w2v2_model* m, const float* pcm, const int32_t* valid, 
                                     m->cfg.conv_stride, vframes, s));
   if (decode)
     W2V2_LAUNCH(m, s, "ctc_collapse",
-                launch_ctc_collapse_keys(m->w.keys, vframes, batch, m->Tf, m->cfg.blank_id, ids, lens, s));
+                launch_ctc_collapse_keys(base.keys, vframes, batch, m->Tf, m->cfg.blank_id, ids, lens, s));
   return W2V2_OK;
 }
 
@@ -758,6 +870,10 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
     for (auto v : e.shape) n *= v;
     for (int64_t j = 0; j < n; ++j)
       if (!std::isfinite(t.data[j])) return fail(W2V2_E_WEIGHTS, "weight " + e.name + " has a non-finite value");
+    static const std::string kAmax = ".input_amax";
+    if (e.name.size() > kAmax.size() && e.name.compare(e.name.size() - kAmax.size(), kAmax.size(), kAmax) == 0 &&
+        !(t.data[0] > 0.f))
+      return fail(W2V2_E_WEIGHTS, "weight " + e.name + " must be positive");
   }
   if ((size_t)n_weights != exp.size()) {
     for (const auto& kv : got) {
@@ -786,7 +902,8 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
   w2v2_model* m = new w2v2_model();
   m->cfg = c;
   m->device = device;
-  m->dt = c.precision == W2V2_FP16 ? DType::F16 : DType::F32;
+  m->dt = (c.precision == W2V2_FP32 || c.precision == W2V2_FP8_ON_FP32) ? DType::F32 : DType::F16;
+  m->fp8 = c.precision == W2V2_FP8 || c.precision == W2V2_FP8_ON_FP32;
   m->act = c.gelu_kind == W2V2_GELU_TANH ? 2 : 1;
   {
     int64_t n = c.window;
@@ -868,6 +985,7 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
   const size_t o_encb = add_f32(ar, Wv("enc.norm.bias", d));
   struct LOff {
     size_t wqkv, wo, w1, w2, bqkv, bo, b1, b2, g1, be1, g2, be2;
+    size_t cs[4] = {0, 0, 0, 0};
   };
   std::vector<LOff> loff(c.layers);
   for (int l = 0; l < c.layers; ++l) {
@@ -878,15 +996,34 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
       memcpy(qkv.data() + (size_t)j * d * d, W(p + "attn." + pr[j] + ".weight"), sizeof(float) * d * d);
       memcpy(bq.data() + (size_t)j * d, W(p + "attn." + pr[j] + ".bias"), sizeof(float) * d);
     }
-    loff[l].wqkv = add_t(ar, dt, qkv);
+    if (m->fp8) {
+      // per-tensor weight scales of q, k and v; the activation scale of
+      // their shared input
+      std::vector<double> sw(3);
+      for (int j = 0; j < 3; ++j) sw[j] = amax_of(qkv.data() + (size_t)j * d * d, (size_t)d * d) / 448.0;
+      loff[l].wqkv = add_e4m3(ar, qkv, {sw[0], sw[1], sw[2]}, (size_t)d * d);
+      const double ax = W(p + "attn.qkv.input_amax")[0];
+      std::vector<float> cs((size_t)3 * d);
+      for (int j = 0; j < 3; ++j)
+        for (int n = 0; n < d; ++n) cs[(size_t)j * d + n] = (float)(ax / 448.0 * sw[j]);
+      loff[l].cs[0] = add_f32(ar, cs);
+    } else {
+      loff[l].wqkv = add_t(ar, dt, qkv);
+    }
     loff[l].bqkv = add_f32(ar, bq);
-    loff[l].wo = add_t(ar, dt, Wv(p + "attn.out.weight", (size_t)d * d));
+    loff[l].wo = m->fp8 ? add_fp8_linear(ar, Wv(p + "attn.out.weight", (size_t)d * d), W(p + "attn.out.input_amax")[0],
+                                         d, &loff[l].cs[1])
+                        : add_t(ar, dt, Wv(p + "attn.out.weight", (size_t)d * d));
     loff[l].bo = add_f32(ar, Wv(p + "attn.out.bias", d));
     loff[l].g1 = add_f32(ar, Wv(p + "attn_norm.weight", d));
     loff[l].be1 = add_f32(ar, Wv(p + "attn_norm.bias", d));
-    loff[l].w1 = add_t(ar, dt, Wv(p + "ffn.fc1.weight", (size_t)F * d));
+    loff[l].w1 = m->fp8 ? add_fp8_linear(ar, Wv(p + "ffn.fc1.weight", (size_t)F * d), W(p + "ffn.fc1.input_amax")[0],
+                                         F, &loff[l].cs[2])
+                        : add_t(ar, dt, Wv(p + "ffn.fc1.weight", (size_t)F * d));
     loff[l].b1 = add_f32(ar, Wv(p + "ffn.fc1.bias", F));
-    loff[l].w2 = add_t(ar, dt, Wv(p + "ffn.fc2.weight", (size_t)d * F));
+    loff[l].w2 = m->fp8 ? add_fp8_linear(ar, Wv(p + "ffn.fc2.weight", (size_t)d * F), W(p + "ffn.fc2.input_amax")[0],
+                                         d, &loff[l].cs[3])
+                        : add_t(ar, dt, Wv(p + "ffn.fc2.weight", (size_t)d * F));
     loff[l].b2 = add_f32(ar, Wv(p + "ffn.fc2.bias", d));
     loff[l].g2 = add_f32(ar, Wv(p + "ffn_norm.weight", d));
     loff[l].be2 = add_f32(ar, Wv(p + "ffn_norm.bias", d));
@@ -935,6 +1072,13 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
     L.ln1_b = PF(loff[l].be1);
     L.ln2_g = PF(loff[l].g2);
     L.ln2_b = PF(loff[l].be2);
+    if (m->fp8) {
+      const std::string p = "layer" + std::to_string(l) + ".";
+      for (int k = 0; k < 4; ++k) {
+        L.cs[k] = PF(loff[l].cs[k]);
+        L.inv[k] = (float)(448.0 / (double)W(p + kFp8Inputs[k] + ".input_amax")[0]);
+      }
+    }
   }
   m->head_w = P(o_hw);
   m->head_b = PF(o_hb);
@@ -1066,6 +1210,17 @@ w2v2_status w2v2_forward_greedy(w2v2_model* m, const float* pcm, const int32_t* 
                                 float* logits, int32_t* vframes, int32_t* ids, int32_t* lens, void* stream) {
   if (!vframes || !ids || !lens) return fail(W2V2_E_ARG, "vframes, ids and lens must not be NULL");
   return forward_impl(m, pcm, valid, batch, logits, vframes, ids, lens, stream);
+}
+
+w2v2_status w2v2_calibrate(w2v2_model* m, const float* pcm, const int32_t* valid, int32_t batch, float* logits,
+                           float* amax, void* stream) {
+  if (!m) return fail(W2V2_E_ARG, "model is NULL");
+  if (!amax) return fail(W2V2_E_ARG, "amax is NULL");
+  if (m->fp8) return fail(W2V2_E_ARG, "calibrate with an fp32 or fp16 model, not an fp8 one");
+  m->calib = amax;
+  const w2v2_status st = forward_impl(m, pcm, valid, batch, logits, nullptr, nullptr, nullptr, stream);
+  m->calib = nullptr;
+  return st;
 }
 
 w2v2_status w2v2_forward_true_length(w2v2_model* m, const float* pcm, const int32_t* valid_host, int32_t batch,

@@ -40,11 +40,15 @@ __device__ inline void store4<half_t>(half_t* p, float4 v) {
 // NV: float4 groups per lane (C <= 256 * NV).  XT: input type.
 // x may alias y32 / yt (in-place use): every lane reads its whole row slice
 // before writing it, so no restrict qualifiers here.
+// y8 (fp8 mode): e4m3 output y * inv8 instead of yt; amax (calibration):
+// raised to the max |y| of the rows.
 template <typename T, typename XT, int NV>
 __global__ __launch_bounds__(256) void layernorm_kernel(const XT* x, int64_t R, int C,
                                                         const float* __restrict__ gamma,
                                                         const float* __restrict__ beta, float eps,
-                                                        float* y32, T* yt, int act, float2* __restrict__ stats) {
+                                                        float* y32, T* yt, int act, float2* __restrict__ stats,
+                                                        uint8_t* __restrict__ y8, float inv8,
+                                                        float* __restrict__ amax) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= R) return;
@@ -85,6 +89,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const XT* x, int64_t R, 
   }
   const float rstd = rsqrtf(wave_sum(q) * invC + eps);
   if (stats && lane == 0) stats[row] = make_float2(mean, rstd);
+  float vmax = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = 4 * (lane + 64 * i);
@@ -102,20 +107,26 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const XT* x, int64_t R, 
       }
       if (y32) *(float4*)(y32 + row * C + c) = o;
       if (yt) store4<T>(yt + row * C + c, o);
+      if (y8) *(uint32_t*)(y8 + row * C + c) = pack_e4m3x4(o.x, o.y, o.z, o.w, inv8);
+      vmax = fmaxf(vmax, fmaxf(fmaxf(fabsf(o.x), fabsf(o.y)), fmaxf(fabsf(o.z), fabsf(o.w))));
     }
   }
+  if (amax) wave_raise_amax(vmax, amax);
 }
 
 template <typename T, typename XT>
 hipError_t ln_dispatch(const XT* x, int64_t R, int C, const float* g, const float* b, float eps, float* y32,
-                       T* yt, int act, float2* st, hipStream_t s) {
+                       T* yt, int act, float2* st, uint8_t* y8, float inv8, float* amax, hipStream_t s) {
   const dim3 grid((unsigned)((R + 3) / 4)), block(256);
   const int nv = (C + 255) / 256;
-  if (nv <= 1) hipLaunchKernelGGL((layernorm_kernel<T, XT, 1>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act, st);
-  else if (nv == 2) hipLaunchKernelGGL((layernorm_kernel<T, XT, 2>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act, st);
-  else if (nv == 3) hipLaunchKernelGGL((layernorm_kernel<T, XT, 3>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act, st);
-  else if (nv == 4) hipLaunchKernelGGL((layernorm_kernel<T, XT, 4>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act, st);
-  else hipLaunchKernelGGL((layernorm_kernel<T, XT, 8>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act, st);
+#define W2V2_LN(NV) \
+  hipLaunchKernelGGL((layernorm_kernel<T, XT, NV>), grid, block, 0, s, x, R, C, g, b, eps, y32, yt, act, st, y8, inv8, amax)
+  if (nv <= 1) W2V2_LN(1);
+  else if (nv == 2) W2V2_LN(2);
+  else if (nv == 3) W2V2_LN(3);
+  else if (nv == 4) W2V2_LN(4);
+  else W2V2_LN(8);
+#undef W2V2_LN
   return hipGetLastError();
 }
 
@@ -184,15 +195,21 @@ inline int grid_for(int64_t work) {
 
 hipError_t launch_layernorm(DType t, const float* x_f32, const void* x_t, int64_t R, int32_t C,
                             const float* gamma, const float* beta, float eps, float* y_f32, void* y_t,
-                            int32_t act, float2* stats, hipStream_t s) {
+                            int32_t act, float2* stats, hipStream_t s, uint8_t* y8, float inv8, float* amax) {
   if (R <= 0) return hipSuccess;
+  if (y8 && C % 4) return hipErrorInvalidValue;
   if (t == DType::F16) {
-    if (x_f32) return ln_dispatch<half_t, float>(x_f32, R, C, gamma, beta, eps, y_f32, (half_t*)y_t, act, stats, s);
+    if (x_f32)
+      return ln_dispatch<half_t, float>(x_f32, R, C, gamma, beta, eps, y_f32, (half_t*)y_t, act, stats, y8, inv8,
+                                        amax, s);
     return ln_dispatch<half_t, half_t>((const half_t*)x_t, R, C, gamma, beta, eps, y_f32, (half_t*)y_t, act, stats,
-                                       s);
+                                       y8, inv8, amax, s);
   }
-  if (x_f32) return ln_dispatch<float, float>(x_f32, R, C, gamma, beta, eps, y_f32, (float*)y_t, act, stats, s);
-  return ln_dispatch<float, float>((const float*)x_t, R, C, gamma, beta, eps, y_f32, (float*)y_t, act, stats, s);
+  if (x_f32)
+    return ln_dispatch<float, float>(x_f32, R, C, gamma, beta, eps, y_f32, (float*)y_t, act, stats, y8, inv8, amax,
+                                     s);
+  return ln_dispatch<float, float>((const float*)x_t, R, C, gamma, beta, eps, y_f32, (float*)y_t, act, stats, y8,
+                                   inv8, amax, s);
 }
 
 hipError_t launch_pos_pack(DType t, const float* h, int32_t B, int32_t T, RowSpan rows, int32_t d, int32_t G,

@@ -258,6 +258,25 @@ w2v2_status w2v2_forward_greedy(w2v2_model* model, const float* pcm, const int32
                                 float* logits, int32_t* vframes, int32_t* ids, int32_t* lens, void* stream);
 
 /*
+ * w2v2_forward_greedy for callers that cannot allocate device memory or
+ * should not touch the model's workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Identical results
+ * (bitwise) to w2v2_forward_greedy, but every intermediate buffer (conv
+ * outputs, GroupNorm partials, residual stream, GEMM operands, argmax keys)
+ * lives in one static device array of the library, 64 MiB, that each GPU the
+ * library runs on holds until the process ends; the call allocates nothing.
+ * Limit: the batch's intermediates must fit in 64 MiB (about 10 one-second
+ * windows of the base network, none of a 16 s one); larger batches are
+ * rejected with W2V2_E_ARG before any device work.  Every call on a GPU
+ * shares that GPU's array (whatever the model), so calls that overlap on one
+ * GPU race: serialize them.
+ * Arguments, stream rules and errors as w2v2_forward_greedy.
+ */
+w2v2_status w2v2_forward_greedy_noalloc(w2v2_model* model, const float* pcm, const int32_t* valid,
+                                        int32_t batch, float* logits, int32_t* vframes, int32_t* ids,
+                                        int32_t* lens, void* stream);
+
+/*
  * Static activation calibration of the fp8 mode ([TRT] "Recipe that was
  * measured": max(abs(input)) of every quantized projection, recorded on the
  * float model over calibration clips).  Runs w2v2_forward on the batch with a

@@ -188,6 +188,24 @@ class Model:
                                                   _ptr(ids), _ptr(lens), _stream(stream)), "w2v2_forward_greedy")
         return logits, vframes, ids, lens
 
+    def forward_greedy_noalloc(self, pcm: torch.Tensor, valid: torch.Tensor, logits: torch.Tensor,
+                               vframes: torch.Tensor, ids: torch.Tensor, lens: torch.Tensor, stream=None):
+        """forward_greedy with every intermediate in the library's static
+        device scratch (``w2v2_forward_greedy_noalloc``): the caller passes
+        all outputs, nothing is allocated."""
+        B = pcm.shape[0]
+        T = self.frames_per_window
+        _need(pcm, torch.float32, (B, self.window), "pcm")
+        _need(valid, torch.int32, (B,), "valid")
+        _need(logits, torch.float32, (B, T, self.vocab), "logits")
+        _need(vframes, torch.int32, (B,), "vframes")
+        _need(ids, torch.int32, (B, T), "ids")
+        _need(lens, torch.int32, (B,), "lens")
+        _lib.check(_lib.lib().w2v2_forward_greedy_noalloc(self._h, _ptr(pcm), _ptr(valid), B, _ptr(logits),
+                                                          _ptr(vframes), _ptr(ids), _ptr(lens), _stream(stream)),
+                   "w2v2_forward_greedy_noalloc")
+        return logits, vframes, ids, lens
+
     def forward_true_length(self, pcm: torch.Tensor, valid, logits: torch.Tensor | None = None,
                             vframes: torch.Tensor | None = None, stream=None):
         """Every row as its own true-length clip of valid[b] samples.

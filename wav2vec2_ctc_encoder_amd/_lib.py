@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
     L.w2v2_forward.restype = i32
     L.w2v2_forward_greedy.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp]
     L.w2v2_forward_greedy.restype = i32
+    L.w2v2_forward_greedy_noalloc.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp]
+    L.w2v2_forward_greedy_noalloc.restype = i32
     L.w2v2_calibrate.argtypes = [vp, vp, vp, i32, vp, vp, vp]
     L.w2v2_calibrate.restype = i32
     L.w2v2_forward_true_length.argtypes = [vp, vp, vp, i32, vp, vp, vp]
@@ -109,7 +111,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("w2v2_create", "w2v2_destroy", "w2v2_num_frames", "w2v2_model_info", "w2v2_forward",
-            "w2v2_forward_greedy", "w2v2_calibrate", "w2v2_forward_true_length", "w2v2_forward_frontend", "w2v2_forward_encoder",
+            "w2v2_forward_greedy", "w2v2_forward_greedy_noalloc", "w2v2_calibrate", "w2v2_forward_true_length", "w2v2_forward_frontend", "w2v2_forward_encoder",
             "w2v2_ctc_greedy", "w2v2_profile_enable", "w2v2_profile_read", "w2v2_last_error")
 
 

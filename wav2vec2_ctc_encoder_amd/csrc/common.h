@@ -116,6 +116,12 @@ __device__ inline float act_fn(float x) {
   else return x;
 }
 
+// Static device scratch (scratch.hip) of the allocation-free entry point:
+// its size, and its device address on `device` (resolved once per device
+// with that device current; call with the device current).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+hipError_t scratch_setup(int device, void** addr);
+
 // Kernel-timing hook of the runtime: called around every launch.
 struct LaunchHook {
   virtual void before(const char* name, hipStream_t s) = 0;

@@ -301,6 +301,7 @@ struct w2v2_model {
   Profiler* prof = nullptr;
   bool prof_on = false;
   bool fp8 = false;           // fp8 mode: e4m3 encoder projections
+  void* scratch = nullptr;    // this device's static scratch (w2v2_forward_greedy_noalloc)
   float* calib = nullptr;     // during w2v2_calibrate: [layers][4] amax slots
   std::string prof_only;  // empty: every kernel
 
@@ -686,7 +687,8 @@ w2v2_status check_forward_args(w2v2_model* m, const void* a, const void* b, int3
 }
 
 // Rows [b0, b0 + n) of every workspace region, as a workspace of its own.
-// base: the whole-batch regions (the model's workspace).
+// base: the whole-batch regions (the model's workspace, or the static
+// scratch laid out for one call's batch).
 Ws ws_rows(const w2v2_model* m, const Ws& base, int b0) {
   auto at = [&](void* p, int i) { return (void*)((uint8_t*)p + (size_t)b0 * m->row_bytes[i]); };
   Ws r;
@@ -705,6 +707,32 @@ Ws ws_rows(const w2v2_model* m, const Ws& base, int b0) {
   return r;
 }
 Ws ws_rows(const w2v2_model* m, int b0) { return ws_rows(m, m->w, b0); }
+
+// The workspace regions of a `batch`-row call packed one after another from
+// `base` (256-byte aligned); *bytes receives their total size.
+Ws ws_packed(const w2v2_model* m, uint8_t* base, int batch, size_t* bytes) {
+  size_t off = 0;
+  void* p[kWsRegions];
+  for (int i = 0; i < kWsRegions; ++i) {
+    p[i] = base + off;
+    off += ((size_t)batch * m->row_bytes[i] + 255) & ~(size_t)255;
+  }
+  *bytes = off;
+  Ws r;
+  r.bufA = p[0];
+  r.bufB = p[1];
+  r.gn_part = (double*)p[2];
+  r.gn_ss = (float2*)p[3];
+  r.h = (float*)p[4];
+  r.x = p[5];
+  r.qkv = p[6];
+  r.attn = p[7];
+  r.ffn = p[8];
+  r.zg = p[9];
+  r.lnst = (float2*)p[10];
+  r.keys = (uint64_t*)p[11];
+  return r;
+}
 
 // Whole network on rows [b0, b0 + n) of the batch, on stream s.
 // decode: the head also raises the rows' argmax keys (w.keys).
@@ -1169,6 +1197,12 @@ w2v2_status w2v2_create(const w2v2_config* cfgp, const w2v2_tensor* weights, int
     delete m;
     return fail(W2V2_E_DEVICE, "hipEventCreate failed");
   }
+  // the device address of this device's static scratch
+  if (scratch_setup(device, &m->scratch) != hipSuccess) {
+    (void)hipGetLastError();
+    delete m;
+    return fail(W2V2_E_DEVICE, "cannot resolve the device address of the static scratch");
+  }
   if (hipDeviceSynchronize() != hipSuccess) {
     delete m;
     return fail(W2V2_E_DEVICE, "device synchronization failed after weight upload");
@@ -1210,6 +1244,21 @@ w2v2_status w2v2_forward_greedy(w2v2_model* m, const float* pcm, const int32_t* 
                                 float* logits, int32_t* vframes, int32_t* ids, int32_t* lens, void* stream) {
   if (!vframes || !ids || !lens) return fail(W2V2_E_ARG, "vframes, ids and lens must not be NULL");
   return forward_impl(m, pcm, valid, batch, logits, vframes, ids, lens, stream);
+}
+
+w2v2_status w2v2_forward_greedy_noalloc(w2v2_model* m, const float* pcm, const int32_t* valid, int32_t batch,
+                                        float* logits, int32_t* vframes, int32_t* ids, int32_t* lens,
+                                        void* stream) {
+  W2V2_TRY(check_forward_args(m, pcm, valid, batch, logits));
+  if (!vframes || !ids || !lens) return fail(W2V2_E_ARG, "vframes, ids and lens must not be NULL");
+  if (!m->scratch) return fail(W2V2_E_DEVICE, "the static scratch has no device address");
+  size_t need = 0;
+  const Ws ws = ws_packed(m, (uint8_t*)m->scratch, batch, &need);
+  if (need > kScratchBytes)
+    return fail(W2V2_E_ARG, "batch " + std::to_string(batch) + " needs " + std::to_string(need) +
+                                " bytes of scratch; w2v2_forward_greedy_noalloc holds " +
+                                std::to_string(kScratchBytes));
+  return forward_impl(m, pcm, valid, batch, logits, vframes, ids, lens, stream, &ws);
 }
 
 w2v2_status w2v2_calibrate(w2v2_model* m, const float* pcm, const int32_t* valid, int32_t batch, float* logits,

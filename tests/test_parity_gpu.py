@@ -507,3 +507,21 @@ def test_forward_greedy_graph_replays_match_eager(name, batch):
             # eager work on other inputs between the replays
             m.forward_greedy(to, tv)
             torch.cuda.synchronize()
+
+
+def test_workspace_beyond_device_memory_is_nomem():
+    """A max_batch whose workspace exceeds the device's memory fails at
+    create with W2V2_E_NOMEM (4096 windows of 16 s need about 390 GB), and
+    the library stays usable."""
+    import wav2vec2_ctc_encoder_amd as w2
+    cfg = synth.BASE_16S_B8.replace(layers=1)
+    W = synth.make_weights(cfg)
+    _say("max_batch 4096 x 16 s: out of device memory")
+    with pytest.raises(w2.W2V2Error) as e:
+        w2.Model(cfg, W, max_batch=4096)
+    assert e.value.status == 4  # W2V2_E_NOMEM
+    with w2.Model(cfg.replace(batch=1), W, max_batch=1) as m:
+        pcm, valid = synth.make_pcm(cfg.replace(batch=1))
+        lg, vf = m.forward(torch.from_numpy(pcm).cuda(), torch.from_numpy(valid).cuda())
+        torch.cuda.synchronize()
+        assert vf.item() == int(oracle.valid_frames(cfg, valid)[0]) and torch.isfinite(lg).all()

@@ -215,12 +215,13 @@ __global__ __launch_bounds__(256) void attention_kernel(const T* __restrict__ qk
 // generic kernel above; K and V^T tiles of 64 keys are double-buffered in
 // LDS with the next tile prefetched into registers, V is transposed with
 // 8-byte LDS writes (4 keys x 4 d per thread), exp2 is the raw hardware
-// instruction and only the last tile is masked.
+// instruction and only the last tile is masked.  The running output is
+// rescaled only on tiles where some query's maximum grew.
 // ----------------------------------------------------------------------------
 // OUT: 0 fp16 output; 1 e4m3 output (fp8 mode); 2 fp16 output and the amax
 // of the calibration (compile-time, so the plain kernel carries neither).
 template <int DH, int NW, int OUT>
-__global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restrict__ qkv, half_t* __restrict__ out,
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DH <= 64 ? 6 : 1))) void attn16_kernel(const half_t* __restrict__ qkv, half_t* __restrict__ out,
                                                         int Tpad, RowSpan rows, int H, float c1,
                                                         uint8_t* __restrict__ out8, float inv8,
                                                         float* __restrict__ amax) {
@@ -295,14 +296,22 @@ __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restric
       const int idx = tid + NT * i;
       if (idx < VGR) {
         const int dg = idx % (DH / 4), kg = idx / (DH / 4);
-        const half_t* e0 = (const half_t*)&rv[i][0];
-        const half_t* e1 = (const half_t*)&rv[i][1];
-        const half_t* e2 = (const half_t*)&rv[i][2];
-        const half_t* e3 = (const half_t*)&rv[i][3];
+        // column dd of the 4 x 4 block (keys kg*4 + r, d = dg*4 + dd) is
+        // half-word dd of rv[i][r]; assembled with shifts and masks, so the
+        // registers are never addressed as memory
 #pragma unroll
         for (int dd = 0; dd < 4; ++dd) {
-          const h4 col = {e0[dd], e1[dd], e2[dd], e3[dd]};
-          *(h4*)&sV[buf][(dg * 4 + dd) * VP + kg * 4] = col;
+          const uint32_t w0 = dd < 2 ? rv[i][0].x : rv[i][0].y, w1 = dd < 2 ? rv[i][1].x : rv[i][1].y;
+          const uint32_t w2 = dd < 2 ? rv[i][2].x : rv[i][2].y, w3 = dd < 2 ? rv[i][3].x : rv[i][3].y;
+          uint2 col;
+          if (dd & 1) {
+            col.x = (w0 >> 16) | (w1 & 0xFFFF0000u);
+            col.y = (w2 >> 16) | (w3 & 0xFFFF0000u);
+          } else {
+            col.x = (w0 & 0xFFFFu) | (w1 << 16);
+            col.y = (w2 & 0xFFFFu) | (w3 << 16);
+          }
+          *(uint2*)&sV[buf][(dg * 4 + dd) * VP + kg * 4] = col;
         }
       }
     }
@@ -349,7 +358,11 @@ __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restric
       mt = max_xor16(mt);
       mt = max_xor32(mt);
       const float mnew = fmaxf(mrun, mt);
-      const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * c1);
+      // Rescale only when some query's running max grew: otherwise every
+      // alpha is exactly 1, o * 1 is o and fma(l, 1, p) is l + p, so the
+      // skip leaves every bit as it was.
+      const bool grew = __builtin_amdgcn_ballot_w64(mnew > mrun) != 0;
+      const float alpha = grew ? __builtin_amdgcn_exp2f((mrun - mnew) * c1) : 1.f;
       const float mc = mnew * c1;
       mrun = mnew;
       float ps = 0.f;
@@ -361,9 +374,13 @@ __global__ __launch_bounds__(NW * 64) void attn16_kernel(const half_t* __restric
           sc[kb][r] = pv;
           ps += pv;
         }
-      lsum = lsum * alpha + ps;
+      if (grew) {
+        lsum = lsum * alpha + ps;
 #pragma unroll
-      for (int i = 0; i < NDB; ++i) o[i] *= alpha;
+        for (int i = 0; i < NDB; ++i) o[i] *= alpha;
+      } else {
+        lsum += ps;
+      }
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
         const h8 pf = {(half_t)sc[2 * kp][0], (half_t)sc[2 * kp][1], (half_t)sc[2 * kp][2], (half_t)sc[2 * kp][3],

@@ -126,10 +126,11 @@ def cpu_baseline(cfg, W, pcm, valid, rows: int, dtype_name: str = "float64") -> 
             "frames_check": int(np.sum(vf))}
 
 
-def read_traffic(kernel: str, key: str = "traffic_bytes_per_launch") -> float | None:
+def read_traffic(kernel: str, workload: str, precision: str,
+                 key: str = "traffic_bytes_per_launch") -> float | None:
     """HBM bytes per launch of `kernel` (its full-batch launches of the
     roofline pass) from a committed rocprofv3 counter summary, if one exists
-    for the current kernel source."""
+    for this workload, precision and the current kernel source."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.txt")
     if not os.path.exists(path):
@@ -147,6 +148,8 @@ def read_traffic(kernel: str, key: str = "traffic_bytes_per_launch") -> float | 
             return None
         h.update(open(src, "rb").read())
     if h.hexdigest()[:16] != kv.get("source_sha16"):
+        return None
+    if kv.get("workload") != workload or kv.get("precision") != precision:
         return None
     try:
         return float(kv[key])
@@ -327,7 +330,7 @@ def main() -> int:
             achieved = per_launch / avg_s / 1e9
             r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
         r["frac"] = round(achieved / r["peak"], 4)
-        r["traffic"] = read_traffic(kernel)
+        r["traffic"] = read_traffic(kernel, cfg.name, cfg.precision)
         r["kernel"] = kernel
         r["avg_launch_ms"] = round(avg_s * 1e3, 4)
         r["launches_per_step"] = launches / steps
@@ -396,10 +399,11 @@ def main() -> int:
             else:
                 ent["gbs"] = round(rate / 1e9, 1)
                 ent["frac_of_peak"] = round(rate / 1e9 / PEAK_HBM_GBS, 4)
-                tr = read_traffic(k)
-                if tr is not None:
-                    ent["traffic_bytes_per_launch"] = tr
-                    ent["traffic_gbs"] = round(tr / (ms / n / 1e3) / 1e9, 1)
+            # HBM-side bytes from the committed counter summary (fp16 kernels of this workload)
+            tr = read_traffic(k, cfg.name, cfg.precision)
+            if tr is not None:
+                ent["traffic_bytes_per_launch"] = tr
+                ent["traffic_gbs"] = round(tr / (ms / n / 1e3) / 1e9, 1)
         kernels[k] = ent
     fe = sum(v["ms_per_step"] for k, v in kernels.items() if k in FRONTEND_KERNELS)
     enc = sum(v["ms_per_step"] for k, v in kernels.items() if k not in FRONTEND_KERNELS)

@@ -33,6 +33,15 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 constexpr int kQ = 64;   // queries per workgroup
 constexpr int kKT = 64;  // keys per tile
 
+// The dispatcher hands consecutive workgroup ids to the 8 XCDs round-robin;
+// this maps them so that each XCD gets one contiguous range of block indices
+// (a bijection for any count).
+__device__ inline int xcd_block(int pid, int nb) {
+  const int x = pid & 7, local = pid >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  return x * per + (x < rem ? x : rem) + local;
+}
+
 template <typename T, int DH>
 struct AttnCfg {
   static constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
@@ -241,14 +250,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DH <= 6
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int b = blockIdx.z, h = blockIdx.y;
+  // 1-D grid of (query block, head, row) in that order, remapped so that the
+  // query blocks of one (row, head), which read the same K and V, run one
+  // after another on one XCD and share its L2
+  const int nqb = (Tpad + NW * 16 - 1) / (NW * 16);
+  const int pid = xcd_block(blockIdx.x, gridDim.x);
+  const int qb = pid % nqb, h = (pid / nqb) % H, b = pid / (nqb * H);
   const int Tn = rows.len ? rows.len[b] : Tpad;                                  // frames of this row
   const int64_t rs = rows.start ? (int64_t)rows.start[b] : (int64_t)b * Tpad;    // its first row
-  if (blockIdx.x * (NW * 16) >= Tn) return;
+  if (qb * (NW * 16) >= Tn) return;
   const int dm = H * DH;
   const int64_t ld = 3 * (int64_t)dm;
   const half_t* base = qkv + rs * ld + h * DH;
-  const int qw = blockIdx.x * (NW * 16) + wave * 16;
+  const int qw = qb * (NW * 16) + wave * 16;
   const bool wave_live = qw < Tn;
 
   uint4 qf[NCH];
@@ -436,7 +450,7 @@ hipError_t launch_a16(const void* qkv, void* out, int B, int Tn, RowSpan rows, i
   constexpr size_t kStatic = 2 * 64 * (DH / 8 + 1) * 16 + 2 * DH * (64 + 4) * 2;  // sK + sV
   constexpr size_t kTwoPerCu = 56 * 1024;
   const size_t pad = (shared && kStatic < kTwoPerCu) ? kTwoPerCu - kStatic : 0;
-  const dim3 grid((Tn + NW * 16 - 1) / (NW * 16), H, B);
+  const dim3 grid(((Tn + NW * 16 - 1) / (NW * 16)) * H * B);
   if (out8)
     hipLaunchKernelGGL((attn16_kernel<DH, NW, 1>), grid, dim3(NW * 64), pad, s, (const half_t*)qkv, (half_t*)out, Tn,
                        rows, H, c1, out8, inv8, amax);

@@ -11,7 +11,7 @@
 //  * the grouped positional conv, one grid.z slice per group, over a
 //    zero-padded per-group copy of its input (lda = C_g, K = taps*C_g).
 //
-// Two kernels, both 256 threads = 4 waves with the weight as the MFMA A
+// Three kernels, all 256 threads = 4 waves with the weight as the MFMA A
 // operand (n side) and the activation as the B operand (m side), so a lane
 // holds consecutive output columns of one row:
 //
@@ -26,6 +26,11 @@
 //   32-row slabs row-major in LDS and writes whole rows (residual add, fp32
 //   and/or fp16 stores), because the 32x32 accumulator layout would
 //   otherwise scatter 16-byte pieces over 32 rows per store.
+//
+// gemm_deep_kernel (fp16 products with K >= 2048 and at most one 128x128
+//   tile per CU: the half-batch FFN2): the same tile and fragment pipeline
+//   with one workgroup per CU, four LDS stages (three in flight) and the
+//   loads of each step spread one per two MFMAs.
 //
 // gemm_kernel (fp32 mode and the remaining shapes): block tile BM x BN, K
 //   step of 128 bytes per row (64 fp16 / 32 fp32), double-buffered LDS with
@@ -782,6 +787,167 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   if (a.out_amax) wave_raise_amax(vmax, a.out_amax);
 }
 
+
+// Long-K products with at most one 128x128 tile per CU (the half-batch FFN2:
+// 150 tiles, K = 3072): one workgroup per CU, four LDS stages with three in
+// flight, and each step's eight loads spread one per two MFMAs, so the wave
+// never stalls behind a burst of load issues.  Every step issues its loads
+// (past the last stage they reload stage nk - 1 into the buffer just
+// vacated, which nobody reads again), so the wait before a step is always
+// "all but the last two stages".
+template <int ROLE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_deep_kernel(GemmArgs a) {
+  constexpr int BM = 128, BN = 128, WN = 2, S = 4;
+  constexpr int TM = 2, TN = 2;
+  constexpr int CPR = 8, RPI = 8, KEYDIV = 2, KS = 4, NF = 4;
+  constexpr int JA = BM / RPI / 4, JB = BN / RPI / 4, LPS = JA + JB;
+  constexpr int ABUF = BM * CPR, BBUF = BN * CPR;
+  static_assert(LPS == 8, "shape");
+
+  __shared__ uint4 smem[S * (ABUF + BBUF)];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles_n = (a.N + BN - 1) / BN;
+  const int pid = xcd_remap(blockIdx.x, gridDim.x);
+  constexpr int GM = 8;
+  const int width = GM * tiles_n;
+  const int first_m = (pid / width) * GM;
+  const int gsz = min(tiles_m - first_m, GM);
+  const int tm = first_m + (pid % width) % gsz;
+  const int tn = (pid % width) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int pos = lane & (CPR - 1);
+  const char* asrc[JA];
+#pragma unroll
+  for (int j = 0; j < JA; ++j) {
+    const int r = (wave * JA + j) * RPI + lane / CPR;
+    const int m = min(m0 + r, a.M - 1);
+    asrc[j] = (const char*)a.A + a_row_offset(a, m) * 2 + ((pos ^ ((r / KEYDIV) & (CPR - 1))) << 4);
+  }
+  const char* bsrc[JB];
+#pragma unroll
+  for (int j = 0; j < JB; ++j) {
+    const int r = (wave * JB + j) * RPI + lane / CPR;
+    const int n = min(n0 + r, a.N - 1);
+    bsrc[j] = (const char*)a.B + (int64_t)n * a.K * 2 + ((pos ^ ((r / KEYDIV) & (CPR - 1))) << 4);
+  }
+  const int nk = a.K / 64;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&smem[0];
+  // load d (0..7) of stage min(kt, nk - 1) into buffer buf
+  auto issue_one = [&](int kt, int buf, int d) {
+    const int64_t koff = (int64_t)min(kt, nk - 1) * 128;
+    if (d < JA)
+      dma16(asrc[d] + koff, __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((buf * ABUF + (wave * JA + d) * 64) * 16)));
+    else
+      dma16(bsrc[d - JA] + koff, __builtin_amdgcn_readfirstlane(
+                                     lds0 + (uint32_t)((S * ABUF + buf * BBUF + (wave * JB + d - JA) * 64) * 16)));
+  };
+
+  const int l32 = lane & 31, lg = lane >> 5;
+  int aoff[NF][TM], boff[NF][TN];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int ch = 2 * f + lg;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int R = wm * TM * 32 + j * 32 + l32;
+      aoff[f][j] = R * CPR + (ch ^ ((R / KEYDIV) & (CPR - 1)));
+    }
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int R = wn * TN * 32 + i * 32 + l32;
+      boff[f][i] = S * ABUF + R * CPR + (ch ^ ((R / KEYDIV) & (CPR - 1)));
+    }
+  }
+
+  f16x acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  uint4 fa0[NF][TM], fb0[NF][TN], fa1[NF][TM], fb1[NF][TN];
+  auto read_frags = [&](int buf, uint4 (&fa)[NF][TM], uint4 (&fb)[NF][TN]) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+#pragma unroll
+      for (int i = 0; i < TN; ++i) fb[f][i] = smem[boff[f][i] + buf * BBUF];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) fa[f][j] = smem[aoff[f][j] + buf * ABUF];
+    }
+  };
+  // step kt (buffer b of stage kt; its fragments are in (fac, fbc)): stage
+  // kt + 1 has landed once all but the last two stages' loads are in; after
+  // the barrier buffer b is refilled with stage kt + S, one load per two
+  // MFMAs, while stage kt + 1's fragments are read between the MFMAs
+  auto step = [&](int kt, int b, int bn, uint4 (&fac)[NF][TM], uint4 (&fbc)[NF][TN], uint4 (&fan)[NF][TM],
+                  uint4 (&fbn)[NF][TN]) {
+    wait_vmcnt_imm<(S - 2) * LPS>();
+    __builtin_amdgcn_s_barrier();
+    int d = 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int i = t / TM, j = t % TM;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, fbc[ks][i]),
+                                                           __builtin_bit_cast(h8, fac[ks][j]), acc[i][j], 0, 0, 0);
+        if ((t & 1) == 0) {
+          issue_one(kt + S, b, d);
+          ++d;
+        }
+        if (t < TN) fbn[ks][t] = smem[boff[ks][t] + bn * BBUF];
+        else fan[ks][t - TN] = smem[aoff[ks][t - TN] + bn * ABUF];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    wait_lgkm0();
+  };
+
+#pragma unroll
+  for (int st = 0; st < S; ++st)
+#pragma unroll
+    for (int d = 0; d < LPS; ++d) issue_one(st, st, d);
+  wait_vmcnt_imm<(S - 2) * LPS>();  // stages 0 and 1
+  __builtin_amdgcn_s_barrier();
+  read_frags(0, fa0, fb0);
+  wait_lgkm0();
+  int kt = 0, b = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    const int b1 = b + 1 == S ? 0 : b + 1;
+    const int b2 = b1 + 1 == S ? 0 : b1 + 1;
+    step(kt, b, b1, fa0, fb0, fa1, fb1);
+    step(kt + 1, b1, b2, fa1, fb1, fa0, fb0);
+    b = b2;
+  }
+  if (kt < nk) step(kt, b, b + 1 == S ? 0 : b + 1, fa0, fb0, fa1, fb1);
+  // the tail's reloads land in buffers the epilogue reuses
+  wait_vmcnt_imm<0>();
+  __builtin_amdgcn_s_barrier();
+
+  constexpr bool NT = ROLE == kGemmConv;
+  float* stage = reinterpret_cast<float*>(smem) + wave * 32 * (TN * 32 + 4);
+  const int m_base = m0 + wm * TM * 32, n_base = n0 + wn * TN * 32;
+  if (a.act == 1) epilogue_staged<TM, TN, 1, NT>(a, acc, stage, m_base, n_base, 0);
+  else if (a.act == 2) epilogue_staged<TM, TN, 2, NT>(a, acc, stage, m_base, n_base, 0);
+  else epilogue_staged<TM, TN, 0, NT>(a, acc, stage, m_base, n_base, 0);
+}
+
+inline bool epilogue_staged_ok_host(const GemmArgs& a) {
+  const uintptr_t ptrs = (uintptr_t)a.out_t | (uintptr_t)a.out_f32 | (uintptr_t)a.residual | (uintptr_t)a.bias |
+                         (uintptr_t)a.res_gamma | (uintptr_t)a.res_beta;
+  return ((a.ldc & 7) == 0) && ((a.N & 7) == 0) && ((a.c_group & 7) == 0) && ((a.bias_group & 7) == 0) &&
+         ((ptrs & 15) == 0) && !a.amax && !a.out_amax;
+}
+
 template <typename T, int BM, int BN, int WM, int WN, int ROLE>
 hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
@@ -825,6 +991,13 @@ hipError_t launch_shape(const GemmArgs& a, hipStream_t s) {
       // short K: out-proj, projection) 128x64 tiles balance the CUs better.
       // The thresholds were measured with the two batch halves of a forward
       // running concurrently (half-batch FFN1 / QKV / FFN2: M = 3196).
+      // long K with at most one tile per CU (half-batch FFN2, 150 tiles):
+      // one deep-pipelined workgroup per CU; same-box A/B of the two-stream
+      // step 3.721 -> 3.674 ms, bit-identical results
+      if (a.N > 64 && a.K >= 2048 && a.groups == 1 && tiles128 <= 256 && epilogue_staged_ok_host(a)) {
+        hipLaunchKernelGGL((gemm_deep_kernel<ROLE>), dim3((unsigned)tiles128), dim3(256), 0, s, a);
+        return hipGetLastError();
+      }
       if (a.N > 64 && (a.N <= 512 || tiles128 >= 400 || (a.K >= 2048 && tiles128 >= 150)))
         return launch_dlds<128, 128, ROLE, 2>(a, s);
       return launch_dlds<128, 64, ROLE, 3>(a, s);

@@ -230,7 +230,7 @@ __device__ inline bool epilogue_staged_ok(const GemmArgs& a) {
 // other instantiations carry neither.
 template <int TM, int TN, int ACT, bool NT, bool F8 = false>
 __device__ inline void epilogue_staged(const GemmArgs& a, f16x (&acc)[TN][TM], float* stage, int m_base,
-                                       int n_base, int group) {
+                                       int n_base, int group, const float* sbias = nullptr, int n0t = 0) {
   constexpr int W = TN * 32;     // columns of the wave block
   constexpr int P = W + 4;       // padded row pitch (floats)
   constexpr int LPR = W / 8;     // lanes per row in the read-back
@@ -251,7 +251,8 @@ __device__ inline void epilogue_staged(const GemmArgs& a, f16x (&acc)[TN][TM], f
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int nc = min(n_base + i * 32 + 8 * q + 4 * lg, a.N - 4);
-      bv[i][q] = bias ? *(const float4*)(bias + nc) : make_float4(0.f, 0.f, 0.f, 0.f);
+      bv[i][q] = sbias  ? *(const float4*)(sbias + (nc - n0t))
+                 : bias ? *(const float4*)(bias + nc) : make_float4(0.f, 0.f, 0.f, 0.f);
       if constexpr (F8) cv[i][q] = cscale ? *(const float4*)(cscale + nc) : make_float4(1.f, 1.f, 1.f, 1.f);
     }
   float vmax = 0.f;  // calibration: max |stored value| of this lane
@@ -528,6 +529,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 __device__ inline void dma16(const void* gptr, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds) : "memory");
 }
+// The same with 4 bytes per lane (lane l's dword lands at lds + 4*l).
+__device__ inline void dma4(const void* gptr, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(gptr), "{m0}"(lds) : "memory");
+}
 
 // s_waitcnt vmcnt(N) with expcnt / lgkmcnt left at their maxima (no wait).
 // Encoding (gfx9): vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
@@ -580,6 +585,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   // [A buffer 0][A buffer 1][B buffer 0][B buffer 1]; the epilogue reuses all of it
   __shared__ uint4 smem[2 * (ABUF + BBUF)];
   static_assert(4 * 32 * (TN * 32 + 4) * 4 <= 2 * (ABUF + BBUF) * 16, "epilogue staging fits");
+  // the tile's bias columns, brought in with the first K step's loads
+  __shared__ float sbias[BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -720,6 +727,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     wait_lgkm0();
   };
 
+  const float* biasg = a.bias ? a.bias + (int64_t)group * a.bias_group : nullptr;
+  if constexpr (!F8) {
+    // wave 0's loads complete in order, so the wait for step 0 below covers these too
+    if (biasg && wave == 0) {
+#pragma unroll
+      for (int h = 0; h < BN / 64; ++h)
+        dma4(biasg + min(n0 + h * 64 + lane, a.N - 1),
+             __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sbias[h * 64]));
+    }
+  }
   issue(0, 0);
   if (nk > 1) {
     issue(1, 1);
@@ -743,9 +760,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     __builtin_amdgcn_s_barrier();
     float* stage = reinterpret_cast<float*>(smem) + wave * 32 * (TN * 32 + 4);
     const int m_base = m0 + wm * TM * 32, n_base = n0 + wn * TN * 32;
-    if (a.act == 1) epilogue_staged<TM, TN, 1, NT, F8>(a, acc, stage, m_base, n_base, group);
-    else if (a.act == 2) epilogue_staged<TM, TN, 2, NT, F8>(a, acc, stage, m_base, n_base, group);
-    else epilogue_staged<TM, TN, 0, NT, F8>(a, acc, stage, m_base, n_base, group);
+    const float* sb = (!F8 && biasg) ? sbias : nullptr;
+    if (a.act == 1) epilogue_staged<TM, TN, 1, NT, F8>(a, acc, stage, m_base, n_base, group, sb, n0);
+    else if (a.act == 2) epilogue_staged<TM, TN, 2, NT, F8>(a, acc, stage, m_base, n_base, group, sb, n0);
+    else epilogue_staged<TM, TN, 0, NT, F8>(a, acc, stage, m_base, n_base, group, sb, n0);
     return;
   }
   const bool vec = epilogue_vec_ok(a);
@@ -805,6 +823,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   static_assert(LPS == 8, "shape");
 
   __shared__ uint4 smem[S * (ABUF + BBUF)];
+  __shared__ float sbias[BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -912,6 +931,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     wait_lgkm0();
   };
 
+  if (a.bias && wave == 0) {
+#pragma unroll
+    for (int h = 0; h < BN / 64; ++h)
+      dma4(a.bias + min(n0 + h * 64 + lane, a.N - 1), __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sbias[h * 64]));
+  }
 #pragma unroll
   for (int st = 0; st < S; ++st)
 #pragma unroll
@@ -936,9 +960,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr bool NT = ROLE == kGemmConv;
   float* stage = reinterpret_cast<float*>(smem) + wave * 32 * (TN * 32 + 4);
   const int m_base = m0 + wm * TM * 32, n_base = n0 + wn * TN * 32;
-  if (a.act == 1) epilogue_staged<TM, TN, 1, NT>(a, acc, stage, m_base, n_base, 0);
-  else if (a.act == 2) epilogue_staged<TM, TN, 2, NT>(a, acc, stage, m_base, n_base, 0);
-  else epilogue_staged<TM, TN, 0, NT>(a, acc, stage, m_base, n_base, 0);
+  const float* sb = a.bias ? sbias : nullptr;
+  if (a.act == 1) epilogue_staged<TM, TN, 1, NT>(a, acc, stage, m_base, n_base, 0, sb, n0);
+  else if (a.act == 2) epilogue_staged<TM, TN, 2, NT>(a, acc, stage, m_base, n_base, 0, sb, n0);
+  else epilogue_staged<TM, TN, 0, NT>(a, acc, stage, m_base, n_base, 0, sb, n0);
 }
 
 inline bool epilogue_staged_ok_host(const GemmArgs& a) {

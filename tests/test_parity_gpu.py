@@ -143,6 +143,10 @@ _TINY_VARIANTS = {
     "head32_window_tail": _TINY.replace(hidden=128, heads=4, window=16000 + 3333, batch=2,
                                         valid_range=(9000, 19333)),
     "head128": _TINY.replace(hidden=256, heads=2, ffn=512, pos_groups=8),
+    # d_h = 64 (the base and large head size) over 153 frames: two query
+    # blocks of 128 and three key tiles of 64, both with a ragged tail
+    "head64_ragged_tiles": _TINY.replace(hidden=128, heads=2, window=3 * 16000 + 1234, batch=3,
+                                         valid_range=(300, 3 * 16000 + 1234)),
     "tanh_gelu_group": _TINY.replace(gelu="tanh", batch=2, valid_range=(8000, 16000)),
     "tanh_gelu_layer_stable": _TINY.replace(gelu="tanh", feat_norm="layer", conv_bias=True, stable_layer_norm=True),
 }
@@ -160,7 +164,7 @@ def test_tiny_fp32_matches_oracle(variant):
     _ids_given_oracle_argmax(cfg, ref, vf_ref)
 
 
-@pytest.mark.parametrize("variant", ["group_postnorm", "layer_stable_bias"])
+@pytest.mark.parametrize("variant", ["group_postnorm", "layer_stable_bias", "head64_ragged_tiles"])
 def test_tiny_fp16_correlates(variant):
     cfg = _TINY_VARIANTS[variant]
     _say(f"tiny fp16 {variant}")

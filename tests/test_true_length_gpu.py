@@ -113,6 +113,36 @@ def test_tiny_fp16_true_length_gates():
     _check_ids(cfg, logits, vf, ids, lens)
 
 
+# d_h = 64 rows whose frame counts sit on the attention tile edges: 1, 2,
+# 64 and 65 frames (one key tile, one more), 128 and 129 (one query block of
+# 128, one more), and the 153-frame window; samples = 400 + 320 (frames - 1)
+_EDGE_FRAMES = [1, 2, 64, 65, 128, 129, 153]
+
+
+def test_head64_fp16_true_length_tile_edges():
+    valid = np.array([0] + [400 + 320 * (f - 1) for f in _EDGE_FRAMES], np.int32)
+    cfg = _TINY.replace(hidden=128, heads=2, window=int(valid[-1]), batch=len(valid), precision="fp16")
+    _say(f"true-length d_h 64 fp16 frames {_EDGE_FRAMES}")
+    pcm = _pcm(cfg, valid)
+    ref, vf_ref = oracle.forward_true_length(cfg, _weights(cfg), pcm, valid)
+    assert vf_ref.tolist() == [0] + _EDGE_FRAMES
+    logits, vf, ids, lens = _gpu_true_length(cfg, pcm, valid, precision="fp16")
+    assert np.array_equal(vf, vf_ref)
+    for i in range(1, len(valid)):
+        n = int(vf[i])
+        r = _pearson(logits[i, :n], ref[i, :n]) if n > 1 else 1.0
+        err = float(np.abs(logits[i, :n].astype(np.float64) - ref[i, :n]).max())
+        _say(f"row {i} frames {n}: pearson {r:.6f} max-abs {err:.3e}")
+        assert r >= 0.999, (i, r)
+    sel_g = np.concatenate([logits[i, :vf[i]] for i in range(len(vf))])
+    sel_r = np.concatenate([ref[i, :vf[i]] for i in range(len(vf))])
+    agree = float(np.mean(np.argmax(sel_g, -1) == np.argmax(sel_r, -1)))
+    _say(f"pooled pearson {_pearson(sel_g, sel_r):.6f} agreement {agree:.5f} over {len(sel_g)} frames")
+    assert _pearson(sel_g, sel_r) >= 0.999 and agree >= 0.995
+    _check_tail_zero(logits, vf)
+    _check_ids(cfg, logits, vf, ids, lens)
+
+
 # base_16s_b32: rows 0 and 31 are the first row of the first half and the
 # last row of the second half of the concurrent split
 @pytest.mark.parametrize("name,rows", [("base_16s_b8", (0, 2, 4, 5)), ("large_16s_b4", (1, 2)),

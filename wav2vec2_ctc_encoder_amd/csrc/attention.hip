@@ -438,6 +438,230 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DH <= 6
   if constexpr (OUT == 2) wave_raise_amax(vmax, amax);
 }
 
+// ----------------------------------------------------------------------------
+// d_h = 64 fp16 kernel with the K and V tiles loaded straight into LDS.
+// Same queries per wave, score layout, softmax and P.V operand order as
+// attn16_kernel (so the results are bit-identical), but:
+//  * each wave moves 8 rows of K and 8 rows of V per 64-key tile with two
+//    wave-wide global_load_lds_dwordx4 (16 bytes per lane), issued two tiles
+//    ahead into a ring of three stages; nothing passes through registers;
+//  * the tiles stay row-major, their 16-byte chunks XOR-swizzled by
+//    (row & 7) so the fragment reads of 16 rows spread over the banks;
+//  * the V^T operand of O^T = V^T P^T comes from gfx950's transposing LDS
+//    read (ds_read_b64_tr_b16): within each 16-lane group g, lane 4j + q
+//    points at V row (4g + j), columns d0 + 4q .. d0 + 4q + 3, and lane i
+//    then receives V[4g + 0..3][d0 + i], four consecutive keys of one
+//    column; two such reads give the eight keys of its k-slots.
+// ----------------------------------------------------------------------------
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+__device__ inline void dma16(const void* gptr, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds) : "memory");
+}
+// s_waitcnt vmcnt(N), other counters untouched
+template <int N>
+__device__ inline void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int NW, int OUT, int S>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(6))) void attn64_kernel(
+    const half_t* __restrict__ qkv, half_t* __restrict__ out, int Tpad, RowSpan rows, int H, float c1,
+    uint8_t* __restrict__ out8, float inv8, float* __restrict__ amax) {
+  constexpr int DH = 64, KT = 64;
+  static_assert(S == 2 || S == 3, "ring of two or three tiles");
+  constexpr int NCH = DH / 32, NDB = DH / 16;
+  constexpr int TILE = KT * DH;  // halves per K (or V) tile
+  static_assert(NW == 8, "one load instruction per wave and operand covers 8 of the 64 rows");
+  __shared__ half_t sK[S][TILE];
+  __shared__ half_t sV[S][TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int nqb = (Tpad + NW * 16 - 1) / (NW * 16);
+  const int pid = xcd_block(blockIdx.x, gridDim.x);
+  const int qb = pid % nqb, h = (pid / nqb) % H, b = pid / (nqb * H);
+  const int Tn = rows.len ? rows.len[b] : Tpad;
+  const int64_t rs = rows.start ? (int64_t)rows.start[b] : (int64_t)b * Tpad;
+  if (qb * (NW * 16) >= Tn) return;
+  const int dm = H * DH;
+  const int64_t ld = 3 * (int64_t)dm;
+  const half_t* base = qkv + rs * ld + h * DH;
+  const int qw = qb * (NW * 16) + wave * 16;
+  const bool wave_live = qw < Tn;
+
+  uint4 qf[NCH];
+  {
+    const int q = min(qw + lr, Tn - 1);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) qf[c] = *(const uint4*)(base + (int64_t)q * ld + c * 32 + lg * 8);
+  }
+
+  // Loads: wave w moves rows 8w .. 8w + 7; lane l takes row 8w + l/8 and puts
+  // its source chunk (l % 8) ^ (row & 7) at chunk l % 8.  Keys past the row's
+  // last frame are read from that frame (their scores are masked).
+  const int lrow = wave * 8 + (lane >> 3);
+  const int lchunk = (lane & 7) ^ (lrow & 7);
+  auto issue = [&](int t) {
+    const int key = min(t * KT + lrow, Tn - 1);
+    const int buf = t % S;
+    const half_t* kp = base + (int64_t)key * ld + dm + lchunk * 8;
+    dma16(kp, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sK[buf][wave * 512]));
+    dma16(kp + dm, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sV[buf][wave * 512]));
+  };
+
+  f4 o[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) o[i] = f4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lsum = 0.f;
+  // per-lane element offsets of the fragment reads (the swizzle depends on
+  // row & 7 only, which the 16-row block offsets keep)
+  int koffs[NCH], voffs[NDB];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) koffs[c] = lr * DH + (((c * 4 + lg) ^ (lr & 7)) << 3);
+  {
+    const int j = lr >> 2, q = lr & 3, vr = 4 * lg + j;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      voffs[db] = vr * DH + ((((db * 16 + 4 * q) >> 3) ^ (vr & 7)) << 3) + ((4 * q) & 7);
+  }
+
+  const int ntile = (Tn + KT - 1) / KT;
+  issue(0);
+  if (S == 3 && ntile > 1) {
+    issue(1);
+    wait_vm<2>();  // tile 0 (this wave's part)
+  } else {
+    wait_vm<0>();
+  }
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    const int cur = t % S;
+    const int k0 = t * KT;
+    // into the buffer of tile t - 1, which every wave finished before the last barrier
+    if (t + S - 1 < ntile) issue(t + S - 1);
+    if (wave_live) {
+      f4 sc[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const uint4 kf = *(const uint4*)&sK[cur][koffs[c] + kb * 16 * DH];
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, kf), __builtin_bit_cast(h8, qf[c]),
+                                                       acc, 0, 0, 0);
+        }
+        sc[kb] = acc;
+      }
+      if (k0 + KT > Tn) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (k0 + kb * 16 + lg * 4 + r >= Tn) sc[kb][r] = -INFINITY;
+      }
+      float mt = sc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sc[kb][r]);
+      mt = max_xor16(mt);
+      mt = max_xor32(mt);
+      const float mnew = fmaxf(mrun, mt);
+      // rescale only when some query's running max grew (else alpha is exactly 1)
+      const bool grew = __builtin_amdgcn_ballot_w64(mnew > mrun) != 0;
+      const float alpha = grew ? __builtin_amdgcn_exp2f((mrun - mnew) * c1) : 1.f;
+      const float mc = mnew * c1;
+      mrun = mnew;
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c1, -mc));
+          sc[kb][r] = pv;
+          ps += pv;
+        }
+      if (grew) {
+        lsum = lsum * alpha + ps;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) o[i] *= alpha;
+      } else {
+        lsum += ps;
+      }
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        const h8 pf = {(half_t)sc[2 * kp][0], (half_t)sc[2 * kp][1], (half_t)sc[2 * kp][2], (half_t)sc[2 * kp][3],
+                       (half_t)sc[2 * kp + 1][0], (half_t)sc[2 * kp + 1][1], (half_t)sc[2 * kp + 1][2],
+                       (half_t)sc[2 * kp + 1][3]};
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          // k-slots 0..3: keys 32kp + 4g + 0..3; 4..7: keys 32kp + 16 + 4g + 0..3
+          v4s part[2];
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s*)&sV[cur][voffs[db] + (kp * 32 + hf * 16) * DH]);
+          const h8 vf = __builtin_bit_cast(h8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, o[db], 0, 0, 0);
+        }
+      }
+    }
+    // this wave's part of tile t + 1 has landed (only tile t + 2's may be out)
+    if (S == 3 && t + 2 < ntile) wait_vm<2>();
+    else wait_vm<0>();
+    __syncthreads();
+  }
+
+  if (!wave_live) return;
+  lsum = add_xor16(lsum);
+  lsum = add_xor32(lsum);
+  const float inv = 1.f / lsum;
+  const int q = qw + lr;
+  float vmax = 0.f;
+  if (q < Tn) {
+    half_t* orow = out + (rs + q) * dm + h * DH;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const float4 ov = make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
+      if constexpr (OUT == 2)
+        vmax = fmaxf(vmax, fmaxf(fmaxf(fabsf(ov.x), fabsf(ov.y)), fmaxf(fabsf(ov.z), fabsf(ov.w))));
+      if constexpr (OUT == 1) {
+        *(uint32_t*)(out8 + (rs + q) * dm + h * DH + db * 16 + lg * 4) = pack_e4m3x4(ov.x, ov.y, ov.z, ov.w, inv8);
+      } else {
+        const h4 hv = {(half_t)ov.x, (half_t)ov.y, (half_t)ov.z, (half_t)ov.w};
+        *(h4*)(orow + db * 16 + lg * 4) = hv;
+      }
+    }
+  }
+  if constexpr (OUT == 2) wave_raise_amax(vmax, amax);
+}
+
+template <int NW, int S>
+hipError_t launch_a64(const void* qkv, void* out, int B, int Tn, RowSpan rows, int H, bool shared, hipStream_t s,
+                      uint8_t* out8, float inv8, float* amax) {
+  const float c1 = 1.4426950408889634f / sqrtf(64.f);
+  // Sharing the chip with the other half's GEMMs, each workgroup takes 48 KB
+  // of LDS: three per CU, or one beside a GEMM workgroup.  Same-box medians
+  // of the two-stream base 8 x 16 s step: 40 KB 3.41 ms, 48 KB 3.41, 56 KB
+  // 3.43, 64 KB 3.45.  A ring of three tiles (two in flight) was slower in
+  // both modes: one-stream attention 0.58 ms against 0.46, step +3.5%.
+  constexpr size_t kStatic = 2 * S * 64 * 64 * 2;  // sK + sV
+  constexpr size_t kShared = 48 * 1024;
+  const size_t pad = (shared && kStatic < kShared) ? kShared - kStatic : 0;
+  const dim3 grid(((Tn + NW * 16 - 1) / (NW * 16)) * H * B);
+  if (out8)
+    hipLaunchKernelGGL((attn64_kernel<NW, 1, S>), grid, dim3(NW * 64), pad, s, (const half_t*)qkv, (half_t*)out, Tn,
+                       rows, H, c1, out8, inv8, amax);
+  else if (amax)
+    hipLaunchKernelGGL((attn64_kernel<NW, 2, S>), grid, dim3(NW * 64), pad, s, (const half_t*)qkv, (half_t*)out, Tn,
+                       rows, H, c1, out8, inv8, amax);
+  else
+    hipLaunchKernelGGL((attn64_kernel<NW, 0, S>), grid, dim3(NW * 64), pad, s, (const half_t*)qkv, (half_t*)out, Tn,
+                       rows, H, c1, out8, inv8, amax);
+  return hipGetLastError();
+}
+
 // shared: another part of the batch runs concurrently.  The kernel then asks
 // for enough (unused) dynamic LDS (56 KB per workgroup) that at most two of
 // its workgroups share a CU, leaving the rest of the CU (48 KB of LDS, one
@@ -493,7 +717,7 @@ hipError_t launch_attention(DType t, const void* qkv, void* out, int32_t B, int3
   if (B <= 0 || T <= 0) return hipSuccess;
   // fp16: 16 queries per wave, 8 waves share each K/V tile
   if (t == DType::F16 && dh == 32) return launch_a16<32, 8>(qkv, out, B, T, rows, H, shared, s, out8, inv8, amax);
-  if (t == DType::F16 && dh == 64) return launch_a16<64, 8>(qkv, out, B, T, rows, H, shared, s, out8, inv8, amax);
+  if (t == DType::F16 && dh == 64) return launch_a64<8, 2>(qkv, out, B, T, rows, H, shared, s, out8, inv8, amax);
   if (t == DType::F16 && dh == 128) return launch_a16<128, 8>(qkv, out, B, T, rows, H, shared, s, out8, inv8, amax);
   return t == DType::F16 ? launch_dh<half_t>(qkv, out, B, T, rows, H, dh, s, out8, inv8, amax)
                          : launch_dh<float>(qkv, out, B, T, rows, H, dh, s, out8, inv8, amax);

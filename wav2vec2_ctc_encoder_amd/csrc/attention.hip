@@ -443,20 +443,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DH <= 6
 // Same queries per wave, score layout, softmax and P.V operand order as
 // attn16_kernel (so the results are bit-identical), but:
 //  * each wave moves 8 rows of K and 8 rows of V per 64-key tile with two
-//    wave-wide global_load_lds_dwordx4 (16 bytes per lane), issued two tiles
-//    ahead into a ring of three stages; nothing passes through registers;
+//    wave-wide global_load_lds_dwordx4 (16 bytes per lane), issued one tile
+//    ahead into a ring of two; nothing passes through registers.  The
+//    address is a wave-uniform tile base in SGPRs plus a loop-invariant
+//    32-bit lane offset, so the loop spends no VALU on it;
 //  * the tiles stay row-major, their 16-byte chunks XOR-swizzled by
 //    (row & 7) so the fragment reads of 16 rows spread over the banks;
 //  * the V^T operand of O^T = V^T P^T comes from gfx950's transposing LDS
 //    read (ds_read_b64_tr_b16): within each 16-lane group g, lane 4j + q
 //    points at V row (4g + j), columns d0 + 4q .. d0 + 4q + 3, and lane i
 //    then receives V[4g + 0..3][d0 + i], four consecutive keys of one
-//    column; two such reads give the eight keys of its k-slots.
+//    column; two such reads give the eight keys of its k-slots;
+//  * the loop is unrolled by two, so the LDS buffers are compile-time.
 // ----------------------------------------------------------------------------
 typedef short v4s __attribute__((ext_vector_type(4)));
 
-__device__ inline void dma16(const void* gptr, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds) : "memory");
+// direct-to-LDS load of 16 bytes per lane from sbase + voff
+__device__ inline void dma16s(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 // s_waitcnt vmcnt(N), other counters untouched
 template <int N>
@@ -464,17 +468,16 @@ __device__ inline void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int NW, int OUT, int S>
+template <int NW, int OUT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(6))) void attn64_kernel(
     const half_t* __restrict__ qkv, half_t* __restrict__ out, int Tpad, RowSpan rows, int H, float c1,
     uint8_t* __restrict__ out8, float inv8, float* __restrict__ amax) {
   constexpr int DH = 64, KT = 64;
-  static_assert(S == 2 || S == 3, "ring of two or three tiles");
   constexpr int NCH = DH / 32, NDB = DH / 16;
   constexpr int TILE = KT * DH;  // halves per K (or V) tile
   static_assert(NW == 8, "one load instruction per wave and operand covers 8 of the 64 rows");
-  __shared__ half_t sK[S][TILE];
-  __shared__ half_t sV[S][TILE];
+  __shared__ half_t sK[2][TILE];
+  __shared__ half_t sV[2][TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -498,16 +501,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(6))) vo
   }
 
   // Loads: wave w moves rows 8w .. 8w + 7; lane l takes row 8w + l/8 and puts
-  // its source chunk (l % 8) ^ (row & 7) at chunk l % 8.  Keys past the row's
-  // last frame are read from that frame (their scores are masked).
+  // its source chunk (l % 8) ^ (row & 7) at chunk l % 8.  Byte offsets are
+  // from the tile's first key row; V sits dm halves after K.  In the last
+  // tile, keys past the row's last frame are read from that frame (their
+  // scores are masked).
   const int lrow = wave * 8 + (lane >> 3);
   const int lchunk = (lane & 7) ^ (lrow & 7);
-  auto issue = [&](int t) {
-    const int key = min(t * KT + lrow, Tn - 1);
-    const int buf = t % S;
-    const half_t* kp = base + (int64_t)key * ld + dm + lchunk * 8;
-    dma16(kp, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sK[buf][wave * 512]));
-    dma16(kp + dm, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sV[buf][wave * 512]));
+  const uint32_t koff = (uint32_t)(lrow * ld + dm + lchunk * 8) * 2u;
+  const uint32_t vdel = (uint32_t)dm * 2u;
+  const uint32_t ldsK = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sK[0][wave * 512]);
+  const uint32_t ldsV = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sV[0][wave * 512]);
+  auto issue = [&](int t, int buf) __attribute__((always_inline)) {
+    const half_t* tb = base + (int64_t)t * KT * ld;
+    uint32_t off = koff;
+    if (t * KT + KT > Tn) {
+      asm volatile("");  // keeps this a branch instead of work in every tile
+      const int key = min(t * KT + lrow, Tn - 1);
+      off = (uint32_t)((key - t * KT) * ld + dm + lchunk * 8) * 2u;
+    }
+    dma16s(off, tb, ldsK + buf * TILE * 2);
+    dma16s(off + vdel, tb, ldsV + buf * TILE * 2);
   };
 
   f4 o[NDB];
@@ -527,19 +540,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(6))) vo
   }
 
   const int ntile = (Tn + KT - 1) / KT;
-  issue(0);
-  if (S == 3 && ntile > 1) {
-    issue(1);
-    wait_vm<2>();  // tile 0 (this wave's part)
-  } else {
-    wait_vm<0>();
-  }
-  __syncthreads();
-  for (int t = 0; t < ntile; ++t) {
-    const int cur = t % S;
+  // one tile from LDS buffer cur; the next tile's loads go to the other one,
+  // which every wave finished with before the previous barrier
+  auto step = [&](int t, int cur) __attribute__((always_inline)) {
     const int k0 = t * KT;
-    // into the buffer of tile t - 1, which every wave finished before the last barrier
-    if (t + S - 1 < ntile) issue(t + S - 1);
+    if (t + 1 < ntile) issue(t + 1, cur ^ 1);
     if (wave_live) {
       f4 sc[4];
 #pragma unroll
@@ -554,6 +559,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(6))) vo
         sc[kb] = acc;
       }
       if (k0 + KT > Tn) {
+        asm volatile("");  // keeps this a branch instead of work in every tile
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -583,6 +589,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(6))) vo
           ps += pv;
         }
       if (grew) {
+        asm volatile("");  // keeps this a branch instead of work in every tile
         lsum = lsum * alpha + ps;
 #pragma unroll
         for (int i = 0; i < NDB; ++i) o[i] *= alpha;
@@ -607,10 +614,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(6))) vo
         }
       }
     }
-    // this wave's part of tile t + 1 has landed (only tile t + 2's may be out)
-    if (S == 3 && t + 2 < ntile) wait_vm<2>();
-    else wait_vm<0>();
+    // this wave's part of tile t + 1 has landed
+    wait_vm<0>();
     __syncthreads();
+  };
+
+  issue(0, 0);
+  wait_vm<0>();
+  __syncthreads();
+  for (int t = 0; t < ntile; t += 2) {
+    step(t, 0);
+    if (t + 1 < ntile) step(t + 1, 1);
   }
 
   if (!wave_live) return;
@@ -637,27 +651,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(6))) vo
   if constexpr (OUT == 2) wave_raise_amax(vmax, amax);
 }
 
-template <int NW, int S>
+template <int NW>
 hipError_t launch_a64(const void* qkv, void* out, int B, int Tn, RowSpan rows, int H, bool shared, hipStream_t s,
                       uint8_t* out8, float inv8, float* amax) {
   const float c1 = 1.4426950408889634f / sqrtf(64.f);
+  // The 32-bit lane offsets of the loads reach 63 rows of the fused q|k|v
+  // matrix past a tile's first row.
+  if ((int64_t)63 * 3 * H * 64 * 2 + 3 * H * 64 * 2 > (int64_t)0xFFFFFFFF) return hipErrorInvalidValue;
   // Sharing the chip with the other half's GEMMs, each workgroup takes 48 KB
   // of LDS: three per CU, or one beside a GEMM workgroup.  Same-box medians
   // of the two-stream base 8 x 16 s step: 40 KB 3.41 ms, 48 KB 3.41, 56 KB
   // 3.43, 64 KB 3.45.  A ring of three tiles (two in flight) was slower in
   // both modes: one-stream attention 0.58 ms against 0.46, step +3.5%.
-  constexpr size_t kStatic = 2 * S * 64 * 64 * 2;  // sK + sV
+  constexpr size_t kStatic = 2 * 2 * 64 * 64 * 2;  // sK + sV
   constexpr size_t kShared = 48 * 1024;
   const size_t pad = (shared && kStatic < kShared) ? kShared - kStatic : 0;
   const dim3 grid(((Tn + NW * 16 - 1) / (NW * 16)) * H * B);
   if (out8)
-    hipLaunchKernelGGL((attn64_kernel<NW, 1, S>), grid, dim3(NW * 64), pad, s, (const half_t*)qkv, (half_t*)out, Tn,
+    hipLaunchKernelGGL((attn64_kernel<NW, 1>), grid, dim3(NW * 64), pad, s, (const half_t*)qkv, (half_t*)out, Tn,
                        rows, H, c1, out8, inv8, amax);
   else if (amax)
-    hipLaunchKernelGGL((attn64_kernel<NW, 2, S>), grid, dim3(NW * 64), pad, s, (const half_t*)qkv, (half_t*)out, Tn,
+    hipLaunchKernelGGL((attn64_kernel<NW, 2>), grid, dim3(NW * 64), pad, s, (const half_t*)qkv, (half_t*)out, Tn,
                        rows, H, c1, out8, inv8, amax);
   else
-    hipLaunchKernelGGL((attn64_kernel<NW, 0, S>), grid, dim3(NW * 64), pad, s, (const half_t*)qkv, (half_t*)out, Tn,
+    hipLaunchKernelGGL((attn64_kernel<NW, 0>), grid, dim3(NW * 64), pad, s, (const half_t*)qkv, (half_t*)out, Tn,
                        rows, H, c1, out8, inv8, amax);
   return hipGetLastError();
 }
@@ -717,7 +734,7 @@ hipError_t launch_attention(DType t, const void* qkv, void* out, int32_t B, int3
   if (B <= 0 || T <= 0) return hipSuccess;
   // fp16: 16 queries per wave, 8 waves share each K/V tile
   if (t == DType::F16 && dh == 32) return launch_a16<32, 8>(qkv, out, B, T, rows, H, shared, s, out8, inv8, amax);
-  if (t == DType::F16 && dh == 64) return launch_a64<8, 2>(qkv, out, B, T, rows, H, shared, s, out8, inv8, amax);
+  if (t == DType::F16 && dh == 64) return launch_a64<8>(qkv, out, B, T, rows, H, shared, s, out8, inv8, amax);
   if (t == DType::F16 && dh == 128) return launch_a16<128, 8>(qkv, out, B, T, rows, H, shared, s, out8, inv8, amax);
   return t == DType::F16 ? launch_dh<half_t>(qkv, out, B, T, rows, H, dh, s, out8, inv8, amax)
                          : launch_dh<float>(qkv, out, B, T, rows, H, dh, s, out8, inv8, amax);

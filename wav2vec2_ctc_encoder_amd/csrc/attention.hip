@@ -4,7 +4,15 @@
 // columns h*dh of each part).  Output: o [B*T, d], heads concatenated.
 // out[q] = sum_key softmax_key(q.k / sqrt(dh)) v[key].
 //
-// Workgroup = 64 queries of one (batch row, head); 4 waves x 16 queries.
+// Three kernels share one score / softmax / P.V formulation:
+//  * attn64_kernel: fp16, d_h = 64 (the base and large models); K and V go
+//    straight from global memory into LDS and V^T is read with the
+//    transposing LDS read;
+//  * attn16_kernel: fp16, d_h = 32 and 128; register-staged tiles with V
+//    transposed on its way into LDS;
+//  * attention_kernel (below): fp32, and head sizes the others do not take.
+//
+// attention_kernel: workgroup = 64 queries of one (batch row, head); 4 waves x 16 queries.
 // K and V are streamed through LDS in tiles of 64 keys (V stored
 // transposed, [d][key]); softmax is computed online in fp32 with exp2 and a
 // running max per query, so the T x T score matrix never leaves registers.

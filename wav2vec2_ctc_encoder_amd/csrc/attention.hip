@@ -5,9 +5,9 @@
 // out[q] = sum_key softmax_key(q.k / sqrt(dh)) v[key].
 //
 // Three kernels share one score / softmax / P.V formulation:
-//  * attn64_kernel: fp16, d_h = 64 (the base and large models); K and V go
-//    straight from global memory into LDS and V^T is read with the
-//    transposing LDS read;
+//  * attn64_kernel: fp16, d_h = 64 (the base and large models); 32 queries
+//    per wave on 32x32x16 MFMAs, K and V go straight from global memory
+//    into LDS and V^T is read with the transposing LDS read;
 //  * attn16_kernel: fp16, d_h = 32 and 128; register-staged tiles with V
 //    transposed on its way into LDS;
 //  * attention_kernel (below): fp32, and head sizes the others do not take.
@@ -447,24 +447,32 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DH <= 6
 }
 
 // ----------------------------------------------------------------------------
-// d_h = 64 fp16 kernel with the K and V tiles loaded straight into LDS.
-// Same queries per wave, score layout, softmax and P.V operand order as
-// attn16_kernel (so the results are bit-identical), but:
-//  * each wave moves 8 rows of K and 8 rows of V per 64-key tile with two
-//    wave-wide global_load_lds_dwordx4 (16 bytes per lane), issued one tile
-//    ahead into a ring of two; nothing passes through registers.  The
-//    address is a wave-uniform tile base in SGPRs plus a loop-invariant
-//    32-bit lane offset, so the loop spends no VALU on it;
-//  * the tiles stay row-major, their 16-byte chunks XOR-swizzled by
-//    (row & 7) so the fragment reads of 16 rows spread over the banks;
-//  * the V^T operand of O^T = V^T P^T comes from gfx950's transposing LDS
-//    read (ds_read_b64_tr_b16): within each 16-lane group g, lane 4j + q
-//    points at V row (4g + j), columns d0 + 4q .. d0 + 4q + 3, and lane i
-//    then receives V[4g + 0..3][d0 + i], four consecutive keys of one
-//    column; two such reads give the eight keys of its k-slots;
+// d_h = 64 fp16 kernel: 32 queries per wave on 32x32x16 MFMAs, with the K
+// and V tiles loaded straight into LDS.  The formulation is attn16_kernel's
+// (S^T = K Q^T, online softmax in fp32 with exp2, P^T fed back as the B
+// operand of O^T = V^T P^T) with bigger blocks:
+//  * a lane holds 16 scores of ONE query (l % 32) per 32-key block, keys
+//    8i + 4(l / 32) + j (i, j = 0..3); a query's row max and sum take one
+//    cross-lane step (lanes l and l ^ 32);
+//  * those registers are already P^T's B operand: for the P.V MFMA u (keys
+//    16u .. 16u + 15 of the block) a lane's k-slots 8(l/32) + 4a + j carry
+//    keys 8(2u + a) + 4(l/32) + j, i.e. its score registers 8u .. 8u + 7;
+//  * the V^T operand (d rows, the same keys) comes from gfx950's transposing
+//    LDS read (ds_read_b64_tr_b16): within each 16-lane group g, lane
+//    4j + q points at V row 8(2u + a) + 4(g / 2) + j, columns
+//    32db + 16(g % 2) + 4q .. + 3, and lane i then receives those 4 keys of
+//    column 32db + 16(g % 2) + i; two reads (a = 0, 1) give the 8 k-slots;
+//  * each K or V fragment read now serves 32 queries (half the LDS reads
+//    per query of 16-query waves);
+//  * every wave moves 16 rows of K and 16 of V per 64-key tile with
+//    wave-wide global_load_lds_dwordx4 (16 bytes per lane), one tile ahead
+//    in a ring of two; the address is a wave-uniform tile base in SGPRs plus
+//    a loop-invariant 32-bit lane offset.  Rows stay row-major with their
+//    16-byte chunks XOR-swizzled by (row & 7);
 //  * the loop is unrolled by two, so the LDS buffers are compile-time.
 // ----------------------------------------------------------------------------
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
 
 // direct-to-LDS load of 16 bytes per lane from sbase + voff
 __device__ inline void dma16s(uint32_t voff, const void* sbase, uint32_t lds) {
@@ -477,109 +485,128 @@ __device__ inline void wait_vm() {
 }
 
 template <int NW, int OUT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(6))) void attn64_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void attn64_kernel(
     const half_t* __restrict__ qkv, half_t* __restrict__ out, int Tpad, RowSpan rows, int H, float c1,
     uint8_t* __restrict__ out8, float inv8, float* __restrict__ amax) {
-  constexpr int DH = 64, KT = 64;
-  constexpr int NCH = DH / 32, NDB = DH / 16;
-  constexpr int TILE = KT * DH;  // halves per K (or V) tile
-  static_assert(NW == 8, "one load instruction per wave and operand covers 8 of the 64 rows");
+  constexpr int DH = 64, KT = 64, TILE = KT * DH;  // halves per K (or V) tile
+  constexpr int QW = 32, QB = NW * QW;             // queries per wave, per workgroup
+  constexpr int RW = KT / NW;                      // tile rows each wave loads
+  static_assert(NW == 4, "16 rows per wave: two load instructions per operand");
   __shared__ half_t sK[2][TILE];
   __shared__ half_t sV[2][TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int nqb = (Tpad + NW * 16 - 1) / (NW * 16);
+  const int l32 = lane & 31, hg = lane >> 5;
+  const int nqb = (Tpad + QB - 1) / QB;
   const int pid = xcd_block(blockIdx.x, gridDim.x);
   const int qb = pid % nqb, h = (pid / nqb) % H, b = pid / (nqb * H);
   const int Tn = rows.len ? rows.len[b] : Tpad;
   const int64_t rs = rows.start ? (int64_t)rows.start[b] : (int64_t)b * Tpad;
-  if (qb * (NW * 16) >= Tn) return;
+  if (qb * QB >= Tn) return;
   const int dm = H * DH;
   const int64_t ld = 3 * (int64_t)dm;
   const half_t* base = qkv + rs * ld + h * DH;
-  const int qw = qb * (NW * 16) + wave * 16;
+  const int qw = qb * QB + wave * QW;
   const bool wave_live = qw < Tn;
 
-  uint4 qf[NCH];
+  // Q^T operand of the score MFMAs: query l32, d = 16c + 8hg .. + 7
+  uint4 qf[4];
   {
-    const int q = min(qw + lr, Tn - 1);
+    const int q = min(qw + l32, Tn - 1);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) qf[c] = *(const uint4*)(base + (int64_t)q * ld + c * 32 + lg * 8);
+    for (int c = 0; c < 4; ++c) qf[c] = *(const uint4*)(base + (int64_t)q * ld + c * 16 + hg * 8);
   }
 
-  // Loads: wave w moves rows 8w .. 8w + 7; lane l takes row 8w + l/8 and puts
-  // its source chunk (l % 8) ^ (row & 7) at chunk l % 8.  Byte offsets are
-  // from the tile's first key row; V sits dm halves after K.  In the last
-  // tile, keys past the row's last frame are read from that frame (their
-  // scores are masked).
-  const int lrow = wave * 8 + (lane >> 3);
-  const int lchunk = (lane & 7) ^ (lrow & 7);
-  const uint32_t koff = (uint32_t)(lrow * ld + dm + lchunk * 8) * 2u;
+  // Loads: wave w moves rows 16w .. 16w + 15, 8 per instruction; lane l takes
+  // row 16w + 8j + l/8 and puts its source chunk (l % 8) ^ (row & 7) at chunk
+  // l % 8.  Byte offsets are from the tile's first key row; V sits dm halves
+  // after K.  In the last tile, keys past the row's last frame are read from
+  // that frame (their scores are masked).
+  const int lr8 = lane >> 3;
+  uint32_t koffj[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = wave * RW + j * 8 + lr8;
+    koffj[j] = (uint32_t)(r * ld + dm + (((lane & 7) ^ (r & 7)) * 8)) * 2u;
+  }
   const uint32_t vdel = (uint32_t)dm * 2u;
-  const uint32_t ldsK = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sK[0][wave * 512]);
-  const uint32_t ldsV = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sV[0][wave * 512]);
+  const uint32_t ldsK = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sK[0][wave * RW * DH]);
+  const uint32_t ldsV = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&sV[0][wave * RW * DH]);
   auto issue = [&](int t, int buf) __attribute__((always_inline)) {
     const half_t* tb = base + (int64_t)t * KT * ld;
-    uint32_t off = koff;
-    if (t * KT + KT > Tn) {
-      asm volatile("");  // keeps this a branch instead of work in every tile
-      const int key = min(t * KT + lrow, Tn - 1);
-      off = (uint32_t)((key - t * KT) * ld + dm + lchunk * 8) * 2u;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t off = koffj[j];
+      if (t * KT + KT > Tn) {
+        asm volatile("");  // keeps this a branch instead of work in every tile
+        const int r = wave * RW + j * 8 + lr8;
+        const int key = min(t * KT + r, Tn - 1);
+        off = (uint32_t)((key - t * KT) * ld + dm + (((lane & 7) ^ (r & 7)) * 8)) * 2u;
+      }
+      dma16s(off, tb, ldsK + (buf * TILE + j * 8 * DH) * 2);
+      dma16s(off + vdel, tb, ldsV + (buf * TILE + j * 8 * DH) * 2);
     }
-    dma16s(off, tb, ldsK + buf * TILE * 2);
-    dma16s(off + vdel, tb, ldsV + buf * TILE * 2);
   };
-
-  f4 o[NDB];
+  // element offsets of the fragment reads (the swizzle depends on row & 7
+  // only, which the block offsets keep)
+  // K operand: key 32kb + l32, d chunk 2c + hg
+  int koffs[4];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) o[i] = f4{0.f, 0.f, 0.f, 0.f};
-  float mrun = -INFINITY, lsum = 0.f;
-  // per-lane element offsets of the fragment reads (the swizzle depends on
-  // row & 7 only, which the 16-row block offsets keep)
-  int koffs[NCH], voffs[NDB];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) koffs[c] = lr * DH + (((c * 4 + lg) ^ (lr & 7)) << 3);
+  for (int c = 0; c < 4; ++c) koffs[c] = l32 * DH + (((2 * c + hg) ^ (l32 & 7)) << 3);
+  // V^T operand: group g, lane i = 4j + q of it: V row 4(g/2) + j (+ 32kb +
+  // 8(2u + a)), columns 32db + 16(g % 2) + 4q .. + 3
+  int voffs[2];
   {
-    const int j = lr >> 2, q = lr & 3, vr = 4 * lg + j;
+    const int g = lane >> 4, jj = (lane & 15) >> 2, q = lane & 3;
+    const int R = 4 * (g >> 1) + jj;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      voffs[db] = vr * DH + ((((db * 16 + 4 * q) >> 3) ^ (vr & 7)) << 3) + ((4 * q) & 7);
+    for (int db = 0; db < 2; ++db) {
+      const int col = db * 32 + 16 * (g & 1) + 4 * q;
+      voffs[db] = R * DH + (((col >> 3) ^ (R & 7)) << 3) + (col & 7);
+    }
   }
 
+  f16v o[2];  // O^T blocks: o[db][r] is d = 32db + 8(r/4) + 4hg + r%4 of query l32
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+  float mrun = -INFINITY, lsum = 0.f;
   const int ntile = (Tn + KT - 1) / KT;
+
   // one tile from LDS buffer cur; the next tile's loads go to the other one,
   // which every wave finished with before the previous barrier
   auto step = [&](int t, int cur) __attribute__((always_inline)) {
     const int k0 = t * KT;
     if (t + 1 < ntile) issue(t + 1, cur ^ 1);
     if (wave_live) {
-      f4 sc[4];
+      f16v sc[2];  // sc[kb][r]: key 32kb + 8(r/4) + 4hg + r%4 of query l32
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 2; ++kb) {
+        f16v acc;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          const uint4 kf = *(const uint4*)&sK[cur][koffs[c] + kb * 16 * DH];
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, kf), __builtin_bit_cast(h8, qf[c]),
-                                                       acc, 0, 0, 0);
+        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint4 kf = *(const uint4*)&sK[cur][koffs[c] + kb * 32 * DH];
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, kf), __builtin_bit_cast(h8, qf[c]), acc,
+                                                       0, 0, 0);
         }
         sc[kb] = acc;
       }
       if (k0 + KT > Tn) {
         asm volatile("");  // keeps this a branch instead of work in every tile
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (k0 + kb * 16 + lg * 4 + r >= Tn) sc[kb][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r)
+            if (k0 + kb * 32 + 8 * (r >> 2) + 4 * hg + (r & 3) >= Tn) sc[kb][r] = -INFINITY;
       }
       float mt = sc[0][0];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sc[kb][r]);
-      mt = max_xor16(mt);
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[kb][r]);
       mt = max_xor32(mt);
       const float mnew = fmaxf(mrun, mt);
       // rescale only when some query's running max grew (else alpha is exactly 1)
@@ -589,9 +616,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(6))) vo
       mrun = mnew;
       float ps = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 16; ++r) {
           const float pv = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c1, -mc));
           sc[kb][r] = pv;
           ps += pv;
@@ -600,27 +627,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(6))) vo
         asm volatile("");  // keeps this a branch instead of work in every tile
         lsum = lsum * alpha + ps;
 #pragma unroll
-        for (int i = 0; i < NDB; ++i) o[i] *= alpha;
+        for (int i = 0; i < 2; ++i) o[i] *= alpha;
       } else {
         lsum += ps;
       }
 #pragma unroll
-      for (int kp = 0; kp < 2; ++kp) {
-        const h8 pf = {(half_t)sc[2 * kp][0], (half_t)sc[2 * kp][1], (half_t)sc[2 * kp][2], (half_t)sc[2 * kp][3],
-                       (half_t)sc[2 * kp + 1][0], (half_t)sc[2 * kp + 1][1], (half_t)sc[2 * kp + 1][2],
-                       (half_t)sc[2 * kp + 1][3]};
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          // k-slots 0..3: keys 32kp + 4g + 0..3; 4..7: keys 32kp + 16 + 4g + 0..3
-          v4s part[2];
+        for (int u = 0; u < 2; ++u) {
+          const h8 pf = {(half_t)sc[kb][8 * u + 0], (half_t)sc[kb][8 * u + 1], (half_t)sc[kb][8 * u + 2],
+                         (half_t)sc[kb][8 * u + 3], (half_t)sc[kb][8 * u + 4], (half_t)sc[kb][8 * u + 5],
+                         (half_t)sc[kb][8 * u + 6], (half_t)sc[kb][8 * u + 7]};
 #pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-            part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4s*)&sV[cur][voffs[db] + (kp * 32 + hf * 16) * DH]);
-          const h8 vf = __builtin_bit_cast(h8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, o[db], 0, 0, 0);
+          for (int db = 0; db < 2; ++db) {
+            v4s part[2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+              part[a] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) v4s*)&sV[cur][voffs[db] + (kb * 32 + 8 * (2 * u + a)) * DH]);
+            const h8 vf = __builtin_bit_cast(h8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[db], 0, 0, 0);
+          }
         }
-      }
     }
     // this wave's part of tile t + 1 has landed
     wait_vm<0>();
@@ -636,25 +664,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(6))) vo
   }
 
   if (!wave_live) return;
-  lsum = add_xor16(lsum);
   lsum = add_xor32(lsum);
   const float inv = 1.f / lsum;
-  const int q = qw + lr;
+  const int q = qw + l32;
   float vmax = 0.f;
   if (q < Tn) {
     half_t* orow = out + (rs + q) * dm + h * DH;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const float4 ov = make_float4(o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv);
-      if constexpr (OUT == 2)
-        vmax = fmaxf(vmax, fmaxf(fmaxf(fabsf(ov.x), fabsf(ov.y)), fmaxf(fabsf(ov.z), fabsf(ov.w))));
-      if constexpr (OUT == 1) {
-        *(uint32_t*)(out8 + (rs + q) * dm + h * DH + db * 16 + lg * 4) = pack_e4m3x4(ov.x, ov.y, ov.z, ov.w, inv8);
-      } else {
-        const h4 hv = {(half_t)ov.x, (half_t)ov.y, (half_t)ov.z, (half_t)ov.w};
-        *(h4*)(orow + db * 16 + lg * 4) = hv;
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = db * 32 + 8 * r4 + 4 * hg;
+        const float4 ov = make_float4(o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv,
+                                      o[db][4 * r4 + 3] * inv);
+        if constexpr (OUT == 2)
+          vmax = fmaxf(vmax, fmaxf(fmaxf(fabsf(ov.x), fabsf(ov.y)), fmaxf(fabsf(ov.z), fabsf(ov.w))));
+        if constexpr (OUT == 1) {
+          *(uint32_t*)(out8 + (rs + q) * dm + h * DH + d0) = pack_e4m3x4(ov.x, ov.y, ov.z, ov.w, inv8);
+        } else {
+          const h4 hv = {(half_t)ov.x, (half_t)ov.y, (half_t)ov.z, (half_t)ov.w};
+          *(h4*)(orow + d0) = hv;
+        }
       }
-    }
   }
   if constexpr (OUT == 2) wave_raise_amax(vmax, amax);
 }
@@ -667,14 +698,13 @@ hipError_t launch_a64(const void* qkv, void* out, int B, int Tn, RowSpan rows, i
   // matrix past a tile's first row.
   if ((int64_t)63 * 3 * H * 64 * 2 + 3 * H * 64 * 2 > (int64_t)0xFFFFFFFF) return hipErrorInvalidValue;
   // Sharing the chip with the other half's GEMMs, each workgroup takes 48 KB
-  // of LDS: three per CU, or one beside a GEMM workgroup.  Same-box medians
-  // of the two-stream base 8 x 16 s step: 40 KB 3.41 ms, 48 KB 3.41, 56 KB
-  // 3.43, 64 KB 3.45.  A ring of three tiles (two in flight) was slower in
-  // both modes: one-stream attention 0.58 ms against 0.46, step +3.5%.
+  // of LDS (three per CU, or one beside a GEMM workgroup); same-box medians
+  // of the two-stream base 8 x 16 s step with 8-wave workgroups of 16-query
+  // waves: 40 KB 3.41 ms, 48 KB 3.41, 56 KB 3.43, 64 KB 3.45.
   constexpr size_t kStatic = 2 * 2 * 64 * 64 * 2;  // sK + sV
   constexpr size_t kShared = 48 * 1024;
   const size_t pad = (shared && kStatic < kShared) ? kShared - kStatic : 0;
-  const dim3 grid(((Tn + NW * 16 - 1) / (NW * 16)) * H * B);
+  const dim3 grid(((Tn + NW * 32 - 1) / (NW * 32)) * H * B);
   if (out8)
     hipLaunchKernelGGL((attn64_kernel<NW, 1>), grid, dim3(NW * 64), pad, s, (const half_t*)qkv, (half_t*)out, Tn,
                        rows, H, c1, out8, inv8, amax);
@@ -742,7 +772,7 @@ hipError_t launch_attention(DType t, const void* qkv, void* out, int32_t B, int3
   if (B <= 0 || T <= 0) return hipSuccess;
   // fp16: 16 queries per wave, 8 waves share each K/V tile
   if (t == DType::F16 && dh == 32) return launch_a16<32, 8>(qkv, out, B, T, rows, H, shared, s, out8, inv8, amax);
-  if (t == DType::F16 && dh == 64) return launch_a64<8>(qkv, out, B, T, rows, H, shared, s, out8, inv8, amax);
+  if (t == DType::F16 && dh == 64) return launch_a64<4>(qkv, out, B, T, rows, H, shared, s, out8, inv8, amax);
   if (t == DType::F16 && dh == 128) return launch_a16<128, 8>(qkv, out, B, T, rows, H, shared, s, out8, inv8, amax);
   return t == DType::F16 ? launch_dh<half_t>(qkv, out, B, T, rows, H, dh, s, out8, inv8, amax)
                          : launch_dh<float>(qkv, out, B, T, rows, H, dh, s, out8, inv8, amax);

@@ -147,6 +147,10 @@ _TINY_VARIANTS = {
     # blocks of 128 and three key tiles of 64, both with a ragged tail
     "head64_ragged_tiles": _TINY.replace(hidden=128, heads=2, window=3 * 16000 + 1234, batch=3,
                                          valid_range=(300, 3 * 16000 + 1234)),
+    # d_h = 64 over 40 s windows: 1999 frames, 16 query blocks and 32 key
+    # tiles per (row, head), longer than any benchmark workload
+    "head64_long_window": _TINY.replace(hidden=128, heads=2, window=40 * 16000, batch=2,
+                                        valid_range=(20 * 16000, 40 * 16000)),
     "tanh_gelu_group": _TINY.replace(gelu="tanh", batch=2, valid_range=(8000, 16000)),
     "tanh_gelu_layer_stable": _TINY.replace(gelu="tanh", feat_norm="layer", conv_bias=True, stable_layer_norm=True),
 }
@@ -164,7 +168,8 @@ def test_tiny_fp32_matches_oracle(variant):
     _ids_given_oracle_argmax(cfg, ref, vf_ref)
 
 
-@pytest.mark.parametrize("variant", ["group_postnorm", "layer_stable_bias", "head64_ragged_tiles"])
+@pytest.mark.parametrize("variant", ["group_postnorm", "layer_stable_bias", "head64_ragged_tiles",
+                                     "head64_long_window"])
 def test_tiny_fp16_correlates(variant):
     cfg = _TINY_VARIANTS[variant]
     _say(f"tiny fp16 {variant}")
